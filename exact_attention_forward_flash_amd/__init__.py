@@ -1,0 +1,11 @@
+"""Exact attention forward on AMD Instinct MI355X (gfx950).
+
+The computation lives in libwf.so (hand-written HIP kernels behind the C ABI declared in
+include/wf.h); this package only loads it and marshals torch tensors to it.
+"""
+from ._lib import ChunkOrderError, CacheConfigError, WfError, load
+from .api import (BlockKVCache, describe, sdpa, varlen_mla_prefill,
+                  varlen_mla_prefill_workspace_size)
+
+__all__ = ["sdpa", "varlen_mla_prefill", "varlen_mla_prefill_workspace_size", "BlockKVCache",
+           "WfError", "ChunkOrderError", "CacheConfigError", "load", "describe"]

@@ -1,0 +1,178 @@
+"""Python surface over libwf.so: torch tensors in, torch tensors out.
+
+Argument marshalling only: shapes and strides are described to the C ABI, outputs and
+workspaces are allocated with torch on the inputs' device, and every computation runs in
+the library's HIP kernels on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import WfBlockKvState, WfTensor, check
+
+_DTYPES = {torch.float32: _lib.WF_F32, torch.float16: _lib.WF_F16, torch.bfloat16: _lib.WF_BF16,
+           torch.bool: _lib.WF_BOOL, torch.int32: _lib.WF_I32}
+
+
+def describe(t: torch.Tensor | None):
+    """A wf_tensor view of a torch tensor (no copy), or None."""
+    if t is None:
+        return None
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d = WfTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _ref(d):
+    return ctypes.byref(d) if d is not None else None
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _scale(scale):
+    return float("nan") if scale is None else float(scale)
+
+
+def sdpa(q, k, v, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
+         return_lse=False):
+    """Exact scaled-dot-product attention forward on the GPU (PyTorch SDPA contract with GQA:
+    q [B,Hq,Lq,Dqk], k [B,Hkv,Lk,Dqk], v [B,Hkv,Lk,Dv]; bool mask = keep, float mask = added
+    to the scaled scores; is_causal is top-left aligned)."""
+    lib = _lib.load()
+    out = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=q.device)
+    lse = None
+    if return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    dq, dk, dv, dm, do = describe(q), describe(k), describe(v), describe(attn_mask), describe(out)
+    lse_ptr = ctypes.cast(lse.data_ptr(), ctypes.POINTER(ctypes.c_float)) if lse is not None and lse.numel() else None
+    check(lib.wf_sdpa_fwd(_ref(dq), _ref(dk), _ref(dv), _ref(dm), int(bool(is_causal)),
+                          float(dropout_p), _scale(scale), _ref(do), lse_ptr, _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def varlen_mla_prefill_workspace_size(batch, total_q_tokens, head_num):
+    return int(_lib.load().wf_varlen_mla_prefill_workspace_size(int(batch), int(total_q_tokens),
+                                                                int(head_num)))
+
+
+def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, kv_head_num,
+                       qk_scale, mask_type=1, workspace=None):
+    """Packed varlen MLA prefill: q [nTq,Hq,128], q_rope [nTq,Hq,64], k/v [nTk,Hkv,128],
+    k_rope [nTk,Hkv,64], device int32 lengths [batch]; mask_type 0 = none, 1 = causal
+    (bottom-right). Returns out [nTq, Hq, 128]."""
+    lib = _lib.load()
+    batch = int(q_seqlen.numel())
+    n_q = q.shape[0]
+    out = torch.empty((n_q, head_num, v.shape[-1]), dtype=q.dtype, device=q.device)
+    need = varlen_mla_prefill_workspace_size(batch, n_q, head_num)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    ds = [describe(t) for t in (q, q_rope, k, k_rope, v, out)]
+    check(lib.wf_varlen_mla_prefill(_ref(ds[0]), _ref(ds[1]), _ref(ds[2]), _ref(ds[3]), _ref(ds[4]),
+                                    ctypes.c_void_p(q_seqlen.data_ptr()),
+                                    ctypes.c_void_p(kv_seqlen.data_ptr()), batch, int(head_num),
+                                    int(kv_head_num), _scale(qk_scale), int(mask_type),
+                                    _ref(ds[5]), ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel(), _stream(q)))
+    return out
+
+
+class BlockKVCache:
+    """Rolling sink + window KV cache (WorldFoundry "Core 注意力", "Block KV cache 的调用顺序").
+
+    Each chunk follows before_update(i) -> update(k, v) -> cached_k()/cached_v() ->
+    after_update(i); i must repeat the current chunk (overwrite) or be the next one.
+    The cache tensors live on `device`; the index bookkeeping is the library's state.
+    """
+
+    def __init__(self, k_shape, v_shape, seq_dim, chunk_size, window_size, sink_size=0,
+                 device="cuda", dtype=torch.float16):
+        self.k_shape, self.v_shape = tuple(k_shape), tuple(v_shape)
+        if len(self.k_shape) != 4 or len(self.v_shape) != 4 or seq_dim not in (1, 2):
+            raise ValueError("4-d cache shapes with seq_dim 1 or 2 (head dim last)")
+        self.seq_dim = seq_dim
+        self.k = torch.zeros(self.k_shape, dtype=dtype, device=device)
+        self.v = torch.zeros(self.v_shape, dtype=dtype, device=device)
+        self.state = WfBlockKvState()
+        check(_lib.load().wf_block_kv_init(ctypes.byref(self.state), self.k_shape[seq_dim],
+                                           int(sink_size), int(window_size), int(chunk_size)))
+        self._pending = None
+
+    def _bhsd(self, t):  # view with the sequence axis third
+        return t if self.seq_dim == 2 else t.transpose(1, 2)
+
+    @property
+    def last_chunk(self):
+        return int(self.state.last_chunk)
+
+    def before_update(self, chunk_idx):
+        self._pending = int(chunk_idx)
+
+    def update(self, k, v):
+        if self._pending is None:
+            raise RuntimeError("update() without before_update()")
+        dk, dv = describe(self._bhsd(k)), describe(self._bhsd(v))
+        dkc, dvc = describe(self._bhsd(self.k)), describe(self._bhsd(self.v))
+        check(_lib.load().wf_block_kv_cache_update(ctypes.byref(self.state), self._pending,
+                                                   _ref(dk), _ref(dv), _ref(dkc), _ref(dvc),
+                                                   _stream(self.k)))
+
+    def after_update(self, chunk_idx):
+        if self._pending != int(chunk_idx):
+            raise RuntimeError("after_update() index differs from before_update()")
+        self._pending = None
+
+    def visible(self):
+        """(n_visible, slot of each visible token in chronological order) from the library."""
+        lib = _lib.load()
+        n = ctypes.c_int64()
+        check(lib.wf_block_kv_visible(ctypes.byref(self.state), ctypes.byref(n), None))
+        idx = (ctypes.c_int64 * max(1, n.value))()
+        check(lib.wf_block_kv_visible(ctypes.byref(self.state), ctypes.byref(n), idx))
+        return n.value, list(idx)[:n.value]
+
+    def _gather(self, cache):
+        n, _ = self.visible()
+        shape = list(self._bhsd(cache).shape)
+        shape[2] = n
+        out = torch.empty(shape, dtype=cache.dtype, device=cache.device)
+        check(_lib.load().wf_block_kv_gather(ctypes.byref(self.state), _ref(describe(self._bhsd(cache))),
+                                             _ref(describe(out)), _stream(cache)))
+        return out if self.seq_dim == 2 else out.transpose(1, 2)
+
+    def cached_k(self):
+        return self._gather(self.k)
+
+    def cached_v(self):
+        return self._gather(self.v)
+
+    def attend(self, q, scale=None, workspace=None):
+        """Non-causal attention of q [B,Hq,Lq,D] over every visible cached token."""
+        lib = _lib.load()
+        kc, vc = self._bhsd(self.k), self._bhsd(self.v)
+        B, Hq, Lq = q.shape[:3]
+        Dv = vc.shape[3]
+        out = torch.empty((B, Hq, Lq, Dv), dtype=q.dtype, device=q.device)
+        need = int(lib.wf_block_kv_attend_workspace_size(ctypes.byref(self.state), B, Hq, Lq, Dv))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        check(lib.wf_block_kv_attend(ctypes.byref(self.state), _ref(describe(q)), _ref(describe(kc)),
+                                     _ref(describe(vc)), _scale(scale), _ref(describe(out)),
+                                     ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                     _stream(q)))
+        return out

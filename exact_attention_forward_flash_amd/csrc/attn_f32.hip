@@ -1,0 +1,160 @@
+// Exact attention forward for fp32 inputs on gfx950 (v_mfma_f32_32x32x2_f32).
+//
+// Same method and transposed formulation as the 16-bit kernel (S^T = K Q^T, O^T += V^T P^T,
+// lane l owns query l % 32, online softmax in fp32), with fp32 operands end to end: P is
+// not rounded before P V. Four waves of 32 queries per work group, 32-key tiles staged
+// through padded LDS rows. The SDPA contract (WorldFoundry "Core 注意力", "选择最窄的入口")
+// and the mask rule after its CPU/GPU example apply unchanged.
+#include "wf_internal.hpp"
+
+namespace wf {
+
+template <int DQK, int DV, int MASK, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_f32_kernel(FwdArgs a) {
+  constexpr int BN = 32, NW = 4, BM = NW * 32;
+  constexpr int KST = DQK + 1;  // padded K row (floats): lanes reading one column hit distinct banks
+  constexpr int NS = DQK / 2, NDV = DV / 32;
+  __shared__ __attribute__((aligned(16))) float Ks[BN * KST];
+  __shared__ __attribute__((aligned(16))) float Vs[BN * DV];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int j = lane & 31, hf = lane >> 5;
+
+  const int t_q = blockIdx.x % a.n_qtiles;
+  const int bh = blockIdx.x / a.n_qtiles;
+  const int hq = bh % a.Hq, b = bh / a.Hq;
+  const int g = hq / a.G;
+  const int qlo = t_q * BM + w * 32;
+  const int qrow = qlo + j;
+  const int qrow_c = qrow < a.Lq ? qrow : a.Lq - 1;
+  const float c = a.scale_log2;
+  const float* qp = (const float*)a.q + b * a.q_sb + hq * a.q_sh + (int64_t)qrow_c * a.q_sm;
+  const float* kp = (const float*)a.k + b * a.k_sb + g * a.k_sh;
+  const float* vp = (const float*)a.v + b * a.v_sb + g * a.v_sh;
+
+  float qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qf[s] = qp[2 * s + hf];
+
+  const char* mrow = nullptr;
+  if constexpr (MASK != MASK_NONE) {
+    constexpr int msz = MASK == MASK_BOOL ? 1 : 4;
+    mrow = (const char*)a.mask + (b * a.mk_sb + hq * a.mk_sh + (int64_t)qrow_c * a.mk_sm) * msz;
+  }
+
+  f32x16 oacc[NDV];
+#pragma unroll
+  for (int n = 0; n < NDV; ++n)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int n_kt = (a.Lk + BN - 1) / BN;
+  int kt_end = n_kt;
+  if (CAUSAL) {
+    const int lim = t_q * BM + BM - 1 + a.causal_shift;
+    kt_end = lim < 0 ? 0 : (lim / BN + 1 < n_kt ? lim / BN + 1 : n_kt);
+  }
+  for (int kt = 0; kt < kt_end; ++kt) {
+    const int k0 = kt * BN;
+    __syncthreads();  // previous tile fully consumed
+    for (int idx = tid * 4; idx < BN * DQK; idx += 256 * 4) {
+      const int r = idx / DQK, col = idx % DQK;
+      const int row = k0 + r < a.Lk ? k0 + r : a.Lk - 1;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(kp + (int64_t)row * a.k_sm + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Ks[r * KST + col + e] = x[e];
+    }
+    for (int idx = tid * 4; idx < BN * DV; idx += 256 * 4) {
+      const int r = idx / DV, col = idx % DV;
+      const int row = k0 + r < a.Lk ? k0 + r : a.Lk - 1;
+      *reinterpret_cast<f32x4*>(&Vs[r * DV + col]) =
+          *reinterpret_cast<const f32x4*>(vp + (int64_t)row * a.v_sm + col);
+    }
+    __syncthreads();
+    if (CAUSAL && k0 > qlo + 31 + a.causal_shift) continue;
+
+    f32x16 sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[j * KST + 2 * s + hf], qf[s], sacc, 0, 0, 0);
+
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      bool ok = key < a.Lk;
+      if (CAUSAL) ok = ok && key <= qrow + a.causal_shift;
+      float t = sacc[r] * c;
+      if constexpr (MASK == MASK_BOOL) {
+        if (ok) ok = mrow[key] != 0;
+      } else if constexpr (MASK == MASK_F32) {
+        if (ok) t += reinterpret_cast<const float*>(mrow)[key] * kLog2e;
+      }
+      t = ok ? t : -INFINITY;
+      sacc[r] = t;
+      mt = fmaxf(mt, t);
+    }
+    mt = xhalf_max(mt);
+    if (wave_any(mt > m_run)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int n = 0; n < NDV; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(sacc[r] + neg_m);
+      sacc[r] = p;
+      l_run += p;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 8 * (r >> 2) + 4 * hf + (r & 3);
+#pragma unroll
+      for (int n = 0; n < NDV; ++n)
+        oacc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * DV + 32 * n + j], sacc[r],
+                                                       oacc[n], 0, 0, 0);
+    }
+  }
+
+  const float l = xhalf_sum(l_run);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  if (qrow < a.Lq) {
+    float* dst = (float*)a.o + b * a.o_sb + hq * a.o_sh + (int64_t)qrow * a.o_sm;
+#pragma unroll
+    for (int n = 0; n < NDV; ++n)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = oacc[n][4 * q4 + e] * inv;
+        *reinterpret_cast<f32x4*>(dst + 32 * n + 8 * q4 + 4 * hf) = o4;
+      }
+    if (a.lse != nullptr && hf == 0)
+      a.lse[((int64_t)b * a.Hq + hq) * a.Lq + qrow] =
+          l > 0.f ? ((m_run == -INFINITY ? 0.f : m_run) + __builtin_log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+#define F(DQK, DV, MASK, CAUSAL) {DQK, DV, MASK, CAUSAL, (const void*)&attn_f32_kernel<DQK, DV, MASK, CAUSAL>, 128}
+#define FD(DQK, DV) F(DQK, DV, MASK_NONE, false), F(DQK, DV, MASK_NONE, true), \
+                    F(DQK, DV, MASK_BOOL, false), F(DQK, DV, MASK_F32, false)
+static const F32Entry kTable[] = {
+    FD(64, 64), FD(64, 96), FD(64, 128), FD(128, 64), FD(128, 96), FD(128, 128),
+};
+#undef FD
+#undef F
+
+const F32Entry* attn_table_f32(int* n) {
+  *n = (int)(sizeof(kTable) / sizeof(kTable[0]));
+  return kTable;
+}
+
+}  // namespace wf

@@ -1,0 +1,483 @@
+// Flash-style exact attention forward for gfx950, 16-bit inputs (bf16 / fp16).
+//
+// Computes out = softmax(scale * Q K^T [+ mask]) V exactly (online softmax, fp32 state)
+// for the PyTorch-SDPA-style call (WorldFoundry "Core 注意力", "选择最窄的入口"), the
+// packed varlen MLA prefill whose score is q.k + qRope.kRope (Ascend "MLA Prefill"
+// parameter table) and the split-KV attend over a block KV cache ("Block KV cache 的调用顺序").
+//
+// Work decomposition
+//   A work group holds HPW query heads of one KV head (GQA) times BMP query positions;
+//   each of its NW waves owns 32 queries of one head. Keys stream through in tiles of
+//   BN = 64, double-buffered in LDS and copied there by direct global->LDS loads.
+//
+// Transposed formulation
+//   Each wave computes S^T = K Q^T (A = K tile from LDS, B = Q^T resident in VGPRs) and
+//   O^T += V^T P^T (A = V^T read from the row-major V tile with ds_read_b64_tr_b16,
+//   B = P^T taken straight from the S^T accumulator). In this layout lane l owns query
+//   l % 32 and half of its keys, so the row max / row sum of the online softmax need no
+//   shuffles inside a half-wave and a single permlane32 swap across halves; O^T is
+//   rescaled by a per-lane factor.
+//
+// Online softmax (log2 domain, t = scale*log2(e)*s [+ log2(e)*mask]):
+//   m is a per-query reference max; p = exp2(t - m); l = sum p; O = sum p v.
+//   m is raised (and O, l rescaled by exp2(m_old - m_new)) only when some query's tile
+//   max exceeds m by more than 8, so p <= 2^8; the result O / l is the same quantity.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so MFMA operand reads hit distinct banks)
+//   K tile row r (a key), chunk c (8 head-dim elements) at chunk position c ^ (r % 8).
+//   V tile row r, chunk c at position c ^ (2 * (r % 4)).
+#pragma once
+#include "wf_device.hpp"
+
+namespace wf {
+
+enum { MASK_NONE = 0, MASK_BOOL = 1, MASK_HALF = 2, MASK_F32 = 3 };
+enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2 };
+
+struct FwdArgs {
+  const void* q; const void* q2; const void* k; const void* k2; const void* v;
+  void* o; float* lse; const void* mask;
+  // strides in elements: batch, head, row (token)
+  int64_t q_sb, q_sh, q_sm, q2_sb, q2_sh, q2_sm;
+  int64_t k_sb, k_sh, k_sm, k2_sb, k2_sh, k2_sm;
+  int64_t v_sb, v_sh, v_sm;
+  int64_t o_sb, o_sh, o_sm;
+  int64_t mk_sb, mk_sh, mk_sm;
+  int B, Hq, Hkv, G, Lq, Lk;
+  int causal_shift;   // key j kept for query i iff j <= i + shift
+  int n_qtiles;       // query tiles per head group (dense / split)
+  int mask_vec;       // mask rows allow 4-element vector loads
+  float scale_log2;   // scale * log2(e)
+  // varlen (persistent) mode
+  const int* cu_q; const int* cu_k; const int2* items; int* counter; const int* n_items;
+  // split-KV mode
+  int tiles_per_split; float* part_o; float* part_lse;
+};
+
+struct WorkItem {
+  int b, hq0, pos0, Lq, Lk, shift, kt_lo, kt_hi, split;
+  int64_t qtok0, ktok0;
+};
+
+template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
+struct AttnFwd {
+  static constexpr int BN = 64;
+  static constexpr int kNW = NW;
+  static constexpr int kHPW = HPW;
+  static constexpr int KCH = DQK / 8;
+  static constexpr int VCH = DV / 8;
+  static constexpr int WPH = NW / HPW;
+  static constexpr int BMP = WPH * 32;
+  static constexpr int NT = NW * 64;
+  static constexpr int KLOADS = BN * KCH / NT;
+  static constexpr int VLOADS = BN * VCH / NT;
+  static constexpr int KBYTES = BN * DQK * 2;
+  static constexpr int VBYTES = BN * DV * 2;
+  static constexpr int NS = DQK / 16;
+  static constexpr int NDV = DV / 32;
+  static_assert(sizeof(T) == 2, "16-bit inputs only");
+  static_assert(NW % HPW == 0, "waves split evenly over heads");
+  static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile copies split evenly");
+  static_assert(KCH % 8 == 0 && VCH % 8 == 0 && DQK1 % 16 == 0 && DV % 32 == 0, "tile shape");
+
+  // Number of key tiles a work group covering positions [pos0, pos0 + BMP) must visit.
+  static __device__ __forceinline__ int tile_end(int pos0, int Lk, int shift) {
+    const int n_kt = (Lk + BN - 1) / BN;
+    if (!CAUSAL) return n_kt;
+    const int lim = pos0 + BMP - 1 + shift;  // last key any query of the group keeps
+    if (lim < 0) return 0;
+    const int e = lim / BN + 1;
+    return e < n_kt ? e : n_kt;
+  }
+
+  static __device__ __forceinline__ void run(const FwdArgs& a, const WorkItem& it,
+                                             WF_LDS char* sK0, WF_LDS char* sK1,
+                                             WF_LDS char* sV0, WF_LDS char* sV1) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, hf = lane >> 5;
+    const int hw = w / WPH;
+    const int qw = (w % WPH) * 32;
+    const int hq = it.hq0 + hw;
+    const int g = it.hq0 / a.G;
+    const float c = a.scale_log2;
+
+    const T* qp = (const T*)a.q + it.b * a.q_sb + hq * a.q_sh + it.qtok0 * a.q_sm;
+    const T* q2p = (const T*)a.q2 + it.b * a.q2_sb + hq * a.q2_sh + it.qtok0 * a.q2_sm;
+    const T* kp = (const T*)a.k + it.b * a.k_sb + g * a.k_sh + it.ktok0 * a.k_sm;
+    const T* k2p = (const T*)a.k2 + it.b * a.k2_sb + g * a.k2_sh + it.ktok0 * a.k2_sm;
+    const T* vp = (const T*)a.v + it.b * a.v_sb + g * a.v_sh + it.ktok0 * a.v_sm;
+
+    // ---- Q^T operand: lane (j, hf) holds query row j, head-dim elements 16s + 8hf.. ----
+    const int qlo = it.pos0 + qw;
+    const int qrow = qlo + j;
+    const int qrow_c = qrow < it.Lq ? qrow : it.Lq - 1;
+    u32x4 qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int col = 16 * s + 8 * hf;
+      const T* src = (16 * s < DQK1) ? qp + (int64_t)qrow_c * a.q_sm + col
+                                     : q2p + (int64_t)qrow_c * a.q2_sm + (col - DQK1);
+      qf[s] = *reinterpret_cast<const u32x4*>(src);
+    }
+
+    // ---- per-thread copy descriptors for the K and V tiles ---------------------------
+    // Copy i of wave w fills tile chunks [(i*NW + w)*64, +64): lane -> chunk p, row p/KCH,
+    // swizzled position p%KCH, which holds logical chunk (p%KCH) ^ swizzle(row).
+    const T* ksrc[KLOADS];
+    int64_t kstride[KLOADS];
+    int krow[KLOADS];
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int p = (i * NW + w) * 64 + lane;
+      const int r = p / KCH, pos = p % KCH;
+      const int col = (pos ^ (r & 7)) * 8;
+      krow[i] = r;
+      if (DQK1 == DQK || col < DQK1) { ksrc[i] = kp + col; kstride[i] = a.k_sm; }
+      else { ksrc[i] = k2p + (col - DQK1); kstride[i] = a.k2_sm; }
+    }
+    const T* vsrc[VLOADS];
+    int vrow[VLOADS];
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int p = (i * NW + w) * 64 + lane;
+      const int r = p / VCH, pos = p % VCH;
+      vrow[i] = r;
+      vsrc[i] = vp + ((pos ^ (2 * (r & 3))) * 8);
+    }
+    const int lk_last = it.Lk - 1;
+    // Rows past the last key are clamped onto it: their scores are masked to -inf, and
+    // the duplicated V rows meet p = 0.
+    auto issue = [&](int kt, WF_LDS char* Kt, WF_LDS char* Vt) {
+      const int k0 = kt * BN;
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i) {
+        int r = k0 + krow[i];
+        r = r < lk_last ? r : lk_last;
+        dma16(ksrc[i] + (int64_t)r * kstride[i], Kt + (i * NW + w) * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < VLOADS; ++i) {
+        int r = k0 + vrow[i];
+        r = r < lk_last ? r : lk_last;
+        dma16(vsrc[i] + (int64_t)r * a.v_sm, Vt + (i * NW + w) * 1024);
+      }
+    };
+
+    // ---- LDS operand offsets ----------------------------------------------------------
+    // K operand (A of S^T): lane (j, hf) reads key row 32kb + j, chunk 2s + hf.
+    int koff[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) koff[s4] = j * KCH * 16 + (((2 * s4 + hf) ^ (j & 7)) * 16);
+    // V^T operand (A of O^T) through the transpose read: within each 16-lane group, lane
+    // s names row kbase + s/4, head-dim columns dbase + 4*(s%4) .. +3, so lane t receives
+    // head-dim dbase + t for the 4 keys kbase .. kbase+3. kbase = 16m + 4hf (+8 for the
+    // second read), dbase = 32n + 16*((lane/16)%2).
+    const int g16 = (lane >> 4) & 1, b2 = (lane & 3) >> 1, fv = 2 * ((lane & 15) >> 2);
+    int voff[2];
+#pragma unroll
+    for (int n2 = 0; n2 < 2; ++n2)
+      voff[n2] = (4 * hf + ((lane & 15) >> 2)) * VCH * 16 +
+                 (((4 * n2 + 2 * g16 + b2) ^ fv) * 16) + 8 * (lane & 1);
+
+    // ---- mask row ---------------------------------------------------------------------
+    const char* mrow = nullptr;
+    if constexpr (MASK != MASK_NONE) {
+      constexpr int msz = MASK == MASK_BOOL ? 1 : MASK == MASK_HALF ? 2 : 4;
+      mrow = (const char*)a.mask +
+             (it.b * a.mk_sb + hq * a.mk_sh + (int64_t)qrow_c * a.mk_sm) * msz;
+    }
+
+    f32x16 oacc[NDV];
+#pragma unroll
+    for (int n = 0; n < NDV; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    auto compute = [&](int kt, const WF_LDS char* Kt, const WF_LDS char* Vt) {
+      const int k0 = kt * BN;
+      if (CAUSAL && k0 > qlo + 31 + it.shift) return;  // every query of this wave is done
+      const bool need_mask = MASK != MASK_NONE || (k0 + BN > it.Lk) ||
+                             (CAUSAL && k0 + BN - 1 > qlo + it.shift);
+
+      // Mask terms (log2 units) for this lane's keys k0 + 32kb + 8q4 + 4hf + e.
+      float mval[2][4][4];
+      if constexpr (MASK != MASK_NONE) {
+        const bool vec = a.mask_vec && (k0 + BN <= it.Lk);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int key = k0 + 32 * kb + 8 * q4 + 4 * hf;
+            if (vec) {
+              if constexpr (MASK == MASK_BOOL) {
+                const uint32_t bits = *reinterpret_cast<const uint32_t*>(mrow + key);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  mval[kb][q4][e] = ((bits >> (8 * e)) & 0xffu) ? 0.f : -INFINITY;
+              } else if constexpr (MASK == MASK_HALF) {
+                typedef T t4 __attribute__((ext_vector_type(4)));
+                const t4 hv = *reinterpret_cast<const t4*>(mrow + 2 * key);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = (float)hv[e] * kLog2e;
+              } else {
+                const f32x4 f4 = *reinterpret_cast<const f32x4*>(mrow + 4 * key);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = f4[e] * kLog2e;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int kk = key + e;
+                float mv = -INFINITY;
+                if (kk < it.Lk) {
+                  if constexpr (MASK == MASK_BOOL) mv = mrow[kk] ? 0.f : -INFINITY;
+                  else if constexpr (MASK == MASK_HALF)
+                    mv = (float)reinterpret_cast<const T*>(mrow)[kk] * kLog2e;
+                  else mv = reinterpret_cast<const float*>(mrow)[kk] * kLog2e;
+                }
+                mval[kb][q4][e] = mv;
+              }
+            }
+          }
+      }
+
+      // S^T = K Q^T: two 32-key blocks, NS steps of 16 head-dim elements each.
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 kop = lds_read16(Kt + koff[s & 3] + (s >> 2) * 128 + kb * 32 * KCH * 16);
+          sacc[kb] = Mfma16<T>::run(kop, qf[s], sacc[kb]);
+        }
+
+      // Online softmax. Element r of block kb is key k0 + 32kb + 8(r/4) + 4hf + r%4.
+      float mt = -INFINITY;
+      if (!need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+        mt *= c;
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            bool ok = key < it.Lk;
+            if (CAUSAL) ok = ok && key <= qrow + it.shift;
+            float t = sacc[kb][r] * c;
+            if constexpr (MASK != MASK_NONE) t += mval[kb][r >> 2][r & 3];
+            t = ok ? t : -INFINITY;
+            sacc[kb][r] = t;
+            mt = fmaxf(mt, t);
+          }
+      }
+      mt = xhalf_max(mt);
+      if (wave_any(mt > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < NDV; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
+        m_run = m_new;
+      }
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      float psum = 0.f;
+      if (!need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sacc[kb][r], c, neg_m));
+            sacc[kb][r] = p;
+            psum += p;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(sacc[kb][r] + neg_m);
+            sacc[kb][r] = p;
+            psum += p;
+          }
+      }
+      l_run += psum;
+
+      // O^T += V^T P^T: 4 steps of 16 keys; step m uses elements 8(m%2).. of block m/2.
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = sacc[m >> 1][8 * (m & 1) + e];
+        const u32x4 pop = pack8<T>(pv);
+#pragma unroll
+        for (int n = 0; n < NDV; ++n) {
+          const WF_LDS char* base = Vt + voff[n & 1] + (n >> 1) * 128 + 16 * m * VCH * 16;
+          const u32x2 lo = lds_read_tr(base);
+          const u32x2 hi = lds_read_tr(base + 8 * VCH * 16);
+          const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
+          oacc[n] = Mfma16<T>::run(vop, pop, oacc[n]);
+        }
+      }
+    };
+
+    // ---- key-tile loop: copy tile kt+1 while computing tile kt -------------------------
+    if (it.kt_lo < it.kt_hi) {
+      issue(it.kt_lo, sK0, sV0);
+      wait_vmem();
+      __syncthreads();
+      int kt = it.kt_lo;
+      for (;;) {
+        if (kt + 1 < it.kt_hi) issue(kt + 1, sK1, sV1);
+        compute(kt, sK0, sV0);
+        wait_vmem();
+        __syncthreads();
+        if (++kt >= it.kt_hi) break;
+        if (kt + 1 < it.kt_hi) issue(kt + 1, sK0, sV0);
+        compute(kt, sK1, sV1);
+        wait_vmem();
+        __syncthreads();
+        if (++kt >= it.kt_hi) break;
+      }
+    }
+
+    // ---- epilogue -----------------------------------------------------------------------
+    const float l = xhalf_sum(l_run);
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float lse2 = l > 0.f ? (m_run == -INFINITY ? 0.f : m_run) + __builtin_log2f(l) : -INFINITY;
+    if (qrow < it.Lq) {
+      if constexpr (MODE == MODE_SPLIT) {
+        const int64_t row = (((int64_t)it.split * a.B + it.b) * a.Hq + hq) * a.Lq + qrow;
+        float* dst = a.part_o + row * DV;
+#pragma unroll
+        for (int n = 0; n < NDV; ++n)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = oacc[n][4 * q4 + e] * inv;
+            *reinterpret_cast<f32x4*>(dst + 32 * n + 8 * q4 + 4 * hf) = o4;
+          }
+        if (hf == 0) a.part_lse[row] = lse2 * kLn2;
+      } else {
+        T* dst = (T*)a.o + it.b * a.o_sb + hq * a.o_sh + (it.qtok0 + qrow) * a.o_sm;
+        typedef T t4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+        for (int n = 0; n < NDV; ++n)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            t4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[n][4 * q4 + e] * inv);
+            *reinterpret_cast<t4*>(dst + 32 * n + 8 * q4 + 4 * hf) = o4;
+          }
+        if (MODE == MODE_DENSE && a.lse != nullptr && hf == 0)
+          a.lse[((int64_t)it.b * a.Hq + hq) * a.Lq + qrow] = lse2 * kLn2;
+      }
+    }
+  }
+};
+
+// Work-group -> work-item decoding for the dense and split grids.
+// Dense: longest-first for causal (query tile rank major), and when B*Hkv is a multiple of
+// 8 the groups sharing one KV head are kept on one XCD (work groups are dealt to the 8 XCDs
+// round-robin by block index), so their K/V tiles are served from that XCD's L2.
+template <class K, bool CAUSAL>
+__device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int split) {
+  const int GH = a.G / K::kHPW;  // head groups per KV head
+  const int nbg = a.B * a.Hkv;
+  int hsub, bg, t_rank;
+  if ((nbg & 7) == 0) {
+    const int x = bid & 7;
+    int s = bid >> 3;
+    hsub = s % GH; s /= GH;
+    const int nbgx = nbg >> 3;
+    bg = (s % nbgx) * 8 + x;
+    t_rank = s / nbgx;
+  } else {
+    hsub = bid % GH;
+    const int s = bid / GH;
+    bg = s % nbg;
+    t_rank = s / nbg;
+  }
+  WorkItem it;
+  const int t = CAUSAL ? a.n_qtiles - 1 - t_rank : t_rank;
+  it.b = bg / a.Hkv;
+  it.hq0 = (bg % a.Hkv) * a.G + hsub * K::kHPW;
+  it.pos0 = t * K::BMP;
+  it.Lq = a.Lq;
+  it.Lk = a.Lk;
+  it.shift = a.causal_shift;
+  it.qtok0 = 0;
+  it.ktok0 = 0;
+  it.split = split;
+  const int end = K::tile_end(it.pos0, it.Lk, it.shift);
+  if (split >= 0) {
+    it.kt_lo = split * a.tiles_per_split;
+    const int hi = it.kt_lo + a.tiles_per_split;
+    it.kt_hi = hi < end ? hi : end;
+  } else {
+    it.kt_lo = 0;
+    it.kt_hi = end;
+  }
+  return it;
+}
+
+template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+  typedef AttnFwd<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE> K;
+  __shared__ __attribute__((aligned(1024))) char sK0[K::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[K::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[K::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[K::VBYTES];
+  WF_LDS char* k0 = (WF_LDS char*)sK0;
+  WF_LDS char* k1 = (WF_LDS char*)sK1;
+  WF_LDS char* v0 = (WF_LDS char*)sV0;
+  WF_LDS char* v1 = (WF_LDS char*)sV1;
+  if constexpr (MODE == MODE_VARLEN) {
+    __shared__ int s_item;
+    const int NHG = a.Hq / HPW;            // head groups per (sequence, query tile) item
+    const int n_work = *a.n_items * NHG;
+    for (;;) {
+      if (threadIdx.x == 0) s_item = atomicAdd(a.counter, 1);
+      __syncthreads();
+      const int idx = s_item;
+      if (idx >= n_work) break;
+      const int2 pr = a.items[idx / NHG];
+      WorkItem it;
+      it.b = pr.x;
+      it.hq0 = (idx % NHG) * HPW;
+      it.pos0 = pr.y * K::BMP;
+      const int cq0 = a.cu_q[it.b], ck0 = a.cu_k[it.b];
+      it.Lq = a.cu_q[it.b + 1] - cq0;
+      it.Lk = a.cu_k[it.b + 1] - ck0;
+      it.qtok0 = cq0;
+      it.ktok0 = ck0;
+      it.shift = CAUSAL ? it.Lk - it.Lq : 0;
+      it.split = -1;
+      it.kt_lo = 0;
+      it.kt_hi = K::tile_end(it.pos0, it.Lk, it.shift);
+      K::run(a, it, k0, k1, v0, v1);
+      __syncthreads();
+    }
+  } else if constexpr (MODE == MODE_SPLIT) {
+    const WorkItem it = decode_grid<K, CAUSAL>(a, blockIdx.x, blockIdx.y);
+    K::run(a, it, k0, k1, v0, v1);
+  } else {
+    const WorkItem it = decode_grid<K, CAUSAL>(a, blockIdx.x, -1);
+    K::run(a, it, k0, k1, v0, v1);
+  }
+}
+
+}  // namespace wf

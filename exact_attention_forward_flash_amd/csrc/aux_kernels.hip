@@ -1,0 +1,304 @@
+// Auxiliary kernels: the varlen tile schedule, the split-KV combine and the block KV cache
+// copy / gather.
+#include "wf_internal.hpp"
+
+namespace wf {
+
+// ------------------------------------------------------------------------------------------
+// Varlen tile schedule (packed sequences given by per-sequence lengths, Ascend "MLA Prefill"
+// qSeqLen / kvSeqLen).
+//   cu_q, cu_k = exclusive prefix sums of the lengths ([batch + 1]);
+//   one work item per (sequence, query tile of bmp positions), ordered by descending
+//   number of key tiles (longest first, so persistent work groups finish together).
+// One work group of 1024 threads; the attention kernel that follows on the stream takes
+// items from the counter this kernel resets.
+// ------------------------------------------------------------------------------------------
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedBuckets = 2048;
+
+__device__ int block_exclusive_scan(int v, int* sm, int* total) {
+  const int t = threadIdx.x;
+  sm[t] = v;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    const int x = t >= off ? sm[t - off] : 0;
+    __syncthreads();
+    sm[t] += x;
+    __syncthreads();
+  }
+  const int incl = sm[t];
+  *total = sm[kSchedThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
+    const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch, int64_t total_q,
+    int64_t total_k, int bmp, int bn, int causal, int max_items, int* ws) {
+  __shared__ int sm[kSchedThreads];
+  __shared__ int hist[kSchedBuckets];
+  __shared__ int s_bad;
+  int* cu_q = (int*)((char*)ws + VarlenWs::cu_q_off());
+  int* cu_k = (int*)((char*)ws + VarlenWs::cu_k_off(batch));
+  int2* items = (int2*)((char*)ws + VarlenWs::items_off(batch));
+  const int t = threadIdx.x;
+  if (t == 0) s_bad = 0;
+  for (int i = t; i < kSchedBuckets; i += kSchedThreads) hist[i] = 0;
+  __syncthreads();
+
+  // Prefix sums over the batch, 1024 sequences at a time. Totals are kept in 64 bits to
+  // reject lengths that overflow.
+  int64_t carry_q = 0, carry_k = 0;
+  int carry_items = 0;
+  for (int base = 0; base < batch; base += kSchedThreads) {
+    const int bi = base + t;
+    int lq = 0, lk = 0;
+    if (bi < batch) {
+      lq = q_seqlen[bi];
+      lk = kv_seqlen[bi];
+      if (lq < 0 || lk < 0) s_bad = 1;
+    }
+    lq = lq < 0 ? 0 : lq;
+    lk = lk < 0 ? 0 : lk;
+    int tot_q, tot_k, tot_i;
+    const int eq = block_exclusive_scan(lq, sm, &tot_q);
+    const int ek = block_exclusive_scan(lk, sm, &tot_k);
+    const int ntile = (lq + bmp - 1) / bmp;
+    block_exclusive_scan(ntile, sm, &tot_i);
+    if (bi < batch) {
+      cu_q[bi] = (int)(carry_q + eq);
+      cu_k[bi] = (int)(carry_k + ek);
+    }
+    carry_q += tot_q;
+    carry_k += tot_k;
+    carry_items += tot_i;
+    __syncthreads();
+  }
+  if (t == 0) {
+    cu_q[batch] = (int)carry_q;
+    cu_k[batch] = (int)carry_k;
+    if (carry_q > total_q || carry_k > total_k || carry_items > max_items) s_bad = 1;
+  }
+  __syncthreads();
+  const int bad = s_bad;
+  const int n_pairs = bad ? 0 : carry_items;
+
+  // Counting sort of the (sequence, query tile) items by descending key-tile count. Pass 0
+  // builds the histogram, then its exclusive scan turns counts into slot offsets; pass 1
+  // places the items. One thread walks the tiles of one sequence.
+  if (!bad) {
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int base = 0; base < batch; base += kSchedThreads) {
+        const int bi = base + t;
+        if (bi < batch) {
+          const int lq = cu_q[bi + 1] - cu_q[bi];
+          const int lk = cu_k[bi + 1] - cu_k[bi];
+          const int ntile = (lq + bmp - 1) / bmp;
+          const int n_kt = (lk + bn - 1) / bn;
+          for (int tt = 0; tt < ntile; ++tt) {
+            int cost = n_kt;
+            if (causal) {
+              const int lim = tt * bmp + bmp - 1 + (lk - lq);
+              cost = lim < 0 ? 0 : (lim / bn + 1 < n_kt ? lim / bn + 1 : n_kt);
+            }
+            const int bucket =
+                kSchedBuckets - 1 - (cost < kSchedBuckets - 1 ? cost : kSchedBuckets - 1);
+            if (pass == 0) {
+              atomicAdd(&hist[bucket], 1);
+            } else {
+              const int pos = atomicAdd(&hist[bucket], 1);
+              items[pos] = make_int2(bi, tt);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (pass == 0) {  // exclusive scan of the histogram; bucket 0 holds the longest items
+        int run = 0;
+        for (int base = 0; base < kSchedBuckets; base += kSchedThreads) {
+          int tot;
+          const int ex = block_exclusive_scan(hist[base + t], sm, &tot);
+          hist[base + t] = run + ex;
+          run += tot;
+          __syncthreads();
+        }
+      }
+    }
+  }
+  if (t == 0) {
+    ws[0] = 0;        // work counter
+    ws[1] = n_pairs;  // number of (sequence, tile) items; heads are expanded by the kernel
+    ws[2] = bad;
+  }
+}
+
+hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
+                                  int64_t total_q, int64_t total_k, int bmp, int bn, int causal,
+                                  int max_items, int* ws, hipStream_t s) {
+  hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, q_seqlen,
+                     kv_seqlen, batch, total_q, total_k, bmp, bn, causal, max_items, ws);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Split-KV combine: out = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max_s lse_s),
+// where O_s is split s's normalised partial output and lse_s its log-sum-exp. A query with
+// no kept key in any split gets 0. Splits are summed in index order (deterministic).
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void split_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, int n_splits,
+    int B, int Hq, int Lq, int Dv, T* out, int64_t o_sb, int64_t o_sh, int64_t o_sm) {
+  const int64_t rows = (int64_t)B * Hq * Lq;
+  const int d4 = Dv / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * d4) return;
+  const int64_t row = gid / d4;
+  const int d = (int)(gid % d4) * 4;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, part_lse[s * rows + row]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < n_splits; ++s) {
+      const float ls = part_lse[s * rows + row];
+      const float wgt = __expf(ls - mx);
+      const f32x4 o = *reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * Dv + d);
+      den += wgt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const int q = (int)(row % Lq);
+  const int hq = (int)((row / Lq) % Hq);
+  const int b = (int)(row / ((int64_t)Lq * Hq));
+  T* dst = out + b * o_sb + hq * o_sh + (int64_t)q * o_sm + d;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[e] = (T)(acc[e] * inv);
+}
+
+hipError_t launch_split_combine(int dtype, const float* part_o, const float* part_lse,
+                                int n_splits, int B, int Hq, int Lq, int Dv, void* out,
+                                int64_t o_sb, int64_t o_sh, int64_t o_sm, hipStream_t s) {
+  const int64_t n = (int64_t)B * Hq * Lq * (Dv / 4);
+  const int blocks = (int)((n + 255) / 256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(split_combine_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, part_o,
+                       part_lse, n_splits, B, Hq, Lq, Dv, (__bf16*)out, o_sb, o_sh, o_sm);
+  else if (dtype == DT_F16)
+    hipLaunchKernelGGL(split_combine_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, part_o,
+                       part_lse, n_splits, B, Hq, Lq, Dv, (_Float16*)out, o_sb, o_sh, o_sm);
+  else
+    hipLaunchKernelGGL(split_combine_kernel<float>, dim3(blocks), dim3(256), 0, s, part_o,
+                       part_lse, n_splits, B, Hq, Lq, Dv, (float*)out, o_sb, o_sh, o_sm);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// Block KV cache ("Block KV cache 的调用顺序": sink prefix never evicted, window rolls).
+// Token t lives in slot t (t < sink) or sink + (t - sink) mod window.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int64_t cache_slot(int64_t t, int64_t sink, int64_t window) {
+  return t < sink ? t : sink + (t - sink) % window;
+}
+
+template <int U> struct CopyUnit;
+template <> struct CopyUnit<16> { typedef u32x4 type; };
+template <> struct CopyUnit<4> { typedef uint32_t type; };
+template <> struct CopyUnit<2> { typedef uint16_t type; };
+
+// Copies one chunk of new rows into their slots, U bytes per thread. Segment 0 is K,
+// segment 1 is V (blockIdx.y). Strides are [b, h, row] in elements.
+template <int U>
+__global__ __launch_bounds__(256) void kv_update_kernel(
+    int esize, const char* k_new, int64_t kn0, int64_t kn1, int64_t kn2, const char* v_new,
+    int64_t vn0, int64_t vn1, int64_t vn2, char* k_cache, int64_t kc0, int64_t kc1, int64_t kc2,
+    char* v_cache, int64_t vc0, int64_t vc1, int64_t vc2, int B, int H, int chunk, int Dk, int Dv,
+    int64_t tok0, int64_t sink, int64_t window) {
+  typedef typename CopyUnit<U>::type unit;
+  const bool isv = blockIdx.y == 1;
+  const int D = isv ? Dv : Dk;
+  const int per_row = D * esize / U;
+  const int64_t n = (int64_t)B * H * chunk * per_row;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n) return;
+  const int piece = (int)(gid % per_row);
+  int64_t r = gid / per_row;
+  const int row = (int)(r % chunk); r /= chunk;
+  const int h = (int)(r % H);
+  const int b = (int)(r / H);
+  const int64_t slot = cache_slot(tok0 + row, sink, window);
+  const char* src = isv ? v_new + (b * vn0 + h * vn1 + row * vn2) * esize
+                        : k_new + (b * kn0 + h * kn1 + row * kn2) * esize;
+  char* dst = isv ? v_cache + (b * vc0 + h * vc1 + slot * vc2) * esize
+                  : k_cache + (b * kc0 + h * kc1 + slot * kc2) * esize;
+  *reinterpret_cast<unit*>(dst + piece * U) = *reinterpret_cast<const unit*>(src + piece * U);
+}
+
+hipError_t launch_kv_update(int unit, int esize, const void* k_new, const int64_t* kn_st,
+                            const void* v_new, const int64_t* vn_st, void* k_cache,
+                            const int64_t* kc_st, void* v_cache, const int64_t* vc_st, int B,
+                            int H, int chunk, int Dk, int Dv, int64_t tok0, int64_t sink,
+                            int64_t window, hipStream_t s) {
+  const int Dmax = Dk > Dv ? Dk : Dv;
+  const int64_t n = (int64_t)B * H * chunk * (Dmax * esize / unit);
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256);
+#define WF_UPD(U)                                                                            \
+  hipLaunchKernelGGL(kv_update_kernel<U>, dim3(blocks, 2), dim3(256), 0, s, esize,           \
+                     (const char*)k_new, kn_st[0], kn_st[1], kn_st[2], (const char*)v_new,   \
+                     vn_st[0], vn_st[1], vn_st[2], (char*)k_cache, kc_st[0], kc_st[1],       \
+                     kc_st[2], (char*)v_cache, vc_st[0], vc_st[1], vc_st[2], B, H, chunk, Dk, \
+                     Dv, tok0, sink, window)
+  if (unit == 16) WF_UPD(16);
+  else if (unit == 4) WF_UPD(4);
+  else WF_UPD(2);
+#undef WF_UPD
+  return hipGetLastError();
+}
+
+// Writes the visible tokens in chronological order: position p < min(T, sink) is token p;
+// the rest are tokens max(sink, T - window) + (p - min(T, sink)).
+template <int U>
+__global__ __launch_bounds__(256) void kv_gather_kernel(
+    int esize, const char* cache, int64_t c0, int64_t c1, int64_t c2, char* out, int64_t o0,
+    int64_t o1, int64_t o2, int B, int H, int64_t n_vis, int D, int64_t T, int64_t sink,
+    int64_t window) {
+  typedef typename CopyUnit<U>::type unit;
+  const int per_row = D * esize / U;
+  const int64_t n = (int64_t)B * H * n_vis * per_row;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= n) return;
+  const int piece = (int)(gid % per_row);
+  int64_t r = gid / per_row;
+  const int64_t p = r % n_vis; r /= n_vis;
+  const int h = (int)(r % H);
+  const int b = (int)(r / H);
+  const int64_t head = T < sink ? T : sink;
+  const int64_t start = (T - window) > sink ? (T - window) : sink;
+  const int64_t tok = p < head ? p : start + (p - head);
+  const int64_t slot = cache_slot(tok, sink, window);
+  const char* src = cache + (b * c0 + h * c1 + slot * c2) * esize;
+  char* dst = out + (b * o0 + h * o1 + p * o2) * esize;
+  *reinterpret_cast<unit*>(dst + piece * U) = *reinterpret_cast<const unit*>(src + piece * U);
+}
+
+hipError_t launch_kv_gather(int unit, int esize, const void* cache, const int64_t* c_st, void* out,
+                            const int64_t* o_st, int B, int H, int64_t n_vis, int D,
+                            int64_t T, int64_t sink, int64_t window, hipStream_t s) {
+  const int64_t n = (int64_t)B * H * n_vis * (D * esize / unit);
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256);
+#define WF_GAT(U)                                                                            \
+  hipLaunchKernelGGL(kv_gather_kernel<U>, dim3(blocks), dim3(256), 0, s, esize,              \
+                     (const char*)cache, c_st[0], c_st[1], c_st[2], (char*)out, o_st[0],     \
+                     o_st[1], o_st[2], B, H, n_vis, D, T, sink, window)
+  if (unit == 16) WF_GAT(16);
+  else if (unit == 4) WF_GAT(4);
+  else WF_GAT(2);
+#undef WF_GAT
+  return hipGetLastError();
+}
+
+}  // namespace wf

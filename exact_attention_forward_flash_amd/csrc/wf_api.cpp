@@ -1,0 +1,594 @@
+// C-ABI entry points (include/wf.h): argument validation, kernel selection from the compiled
+// instantiation tables, launch geometry and the block KV cache state machine.
+// Validation completes before anything is enqueued; a failing call changes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/wf.h"
+#include "wf_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return WF_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(WF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int esize(int dt) {
+  switch (dt) {
+    case WF_F32: return 4;
+    case WF_F16: return 2;
+    case WF_BF16: return 2;
+    case WF_BOOL: return 1;
+    case WF_I32: return 4;
+    default: return 0;
+  }
+}
+
+bool is_float_dt(int dt) { return dt == WF_F32 || dt == WF_F16 || dt == WF_BF16; }
+
+int64_t numel(const wf_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// Checks a data tensor: rank, non-negative shape, inner stride 1, every row start
+// 16-byte aligned (base pointer and all outer strides).
+int check_data(const wf_tensor* t, const char* name, int ndim) {
+  if (t == nullptr) return fail(WF_ERR_NULL, "%s is NULL", name);
+  if (t->ndim != ndim) return fail(WF_ERR_SHAPE, "%s must be %d-d, got %d-d", name, ndim, t->ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(WF_ERR_SHAPE, "%s has a negative dimension", name);
+  if (!is_float_dt(t->dtype)) return fail(WF_ERR_DTYPE, "%s must be f32, f16 or bf16", name);
+  if (numel(t) == 0) return WF_OK;
+  if (t->data == nullptr) return fail(WF_ERR_NULL, "%s->data is NULL", name);
+  if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] != 1)
+    return fail(WF_ERR_LAYOUT, "%s: innermost stride must be 1", name);
+  const int es = esize(t->dtype);
+  const int64_t al = 16 / es;
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0)
+    return fail(WF_ERR_LAYOUT, "%s: data pointer must be 16-byte aligned", name);
+  for (int i = 0; i < ndim - 1; ++i)
+    if (t->shape[i] > 1 && t->stride[i] % al != 0)
+      return fail(WF_ERR_LAYOUT, "%s: stride[%d] = %lld is not a multiple of %lld elements", name,
+                  i, (long long)t->stride[i], (long long)al);
+  if ((t->shape[ndim - 1] * es) % 16 != 0)
+    return fail(WF_ERR_LAYOUT, "%s: rows must be a multiple of 16 bytes", name);
+  return WF_OK;
+}
+
+int64_t st(const wf_tensor* t, int i) { return t->shape[i] == 1 ? 0 : t->stride[i]; }
+
+// Cache copies accept any row width: only the inner stride and element alignment matter.
+// *unit16 is cleared when a tensor does not allow 16-byte copies.
+int check_cache_data(const wf_tensor* t, const char* name, bool* unit16) {
+  if (t == nullptr) return fail(WF_ERR_NULL, "%s is NULL", name);
+  if (t->ndim != 4) return fail(WF_ERR_SHAPE, "%s must be 4-d [B,H,S,D]", name);
+  for (int i = 0; i < 4; ++i)
+    if (t->shape[i] < 0) return fail(WF_ERR_SHAPE, "%s has a negative dimension", name);
+  if (!is_float_dt(t->dtype)) return fail(WF_ERR_DTYPE, "%s must be f32, f16 or bf16", name);
+  if (numel(t) == 0) return WF_OK;
+  if (t->data == nullptr) return fail(WF_ERR_NULL, "%s->data is NULL", name);
+  if (t->stride[3] != 1 && t->shape[3] != 1)
+    return fail(WF_ERR_LAYOUT, "%s: innermost stride must be 1", name);
+  const int es = esize(t->dtype);
+  if (reinterpret_cast<uintptr_t>(t->data) % es != 0)
+    return fail(WF_ERR_LAYOUT, "%s: data pointer is not aligned to its element size", name);
+  if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0 || (t->shape[3] * es) % 16 != 0) *unit16 = false;
+  for (int i = 0; i < 3; ++i)
+    if ((t->stride[i] * es) % 16 != 0) *unit16 = false;
+  return WF_OK;
+}
+
+const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int hpw, int mask,
+                               int causal, int mode) {
+  typedef const wf::AttnEntry* (*TableFn)(int*);
+  static const TableFn tables[] = {wf::attn_table_sdpa_bf16_d64, wf::attn_table_sdpa_bf16_d128,
+                                   wf::attn_table_sdpa_f16_d64,  wf::attn_table_sdpa_f16_d128,
+                                   wf::attn_table_mla,           wf::attn_table_split};
+  for (TableFn f : tables) {
+    int n = 0;
+    const wf::AttnEntry* t = f(&n);
+    for (int i = 0; i < n; ++i) {
+      const wf::AttnEntry& e = t[i];
+      if (e.dtype == dtype && e.dqk == dqk && e.dqk1 == dqk1 && e.dv == dv &&
+          (nw == 0 || e.nw == nw) && (hpw == 0 || e.hpw == hpw) && e.mask == mask &&
+          e.causal == causal && e.mode == mode)
+        return &e;
+    }
+  }
+  return nullptr;
+}
+
+const wf::F32Entry* find_f32(int dqk, int dv, int mask, int causal) {
+  int n = 0;
+  const wf::F32Entry* t = wf::attn_table_f32(&n);
+  for (int i = 0; i < n; ++i)
+    if (t[i].dqk == dqk && t[i].dv == dv && t[i].mask == mask && t[i].causal == causal) return &t[i];
+  return nullptr;
+}
+
+int kernel_dtype(int dt) { return dt == WF_BF16 ? wf::DT_BF16 : dt == WF_F16 ? wf::DT_F16 : wf::DT_F32; }
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+hipError_t launch(const void* fn, dim3 grid, dim3 block, wf::FwdArgs& a, hipStream_t s) {
+  void* args[] = {&a};
+  return hipLaunchKernel(fn, grid, block, args, 0, s);
+}
+
+int resolve_scale(float scale, int64_t dqk, float* out) {
+  if (std::isnan(scale)) {
+    *out = (float)(1.0 / std::sqrt((double)dqk));
+    return WF_OK;
+  }
+  if (!std::isfinite(scale) || scale <= 0.f)
+    return fail(WF_ERR_UNSUPPORTED, "scale must be finite and > 0 (or NaN for 1/sqrt(d))");
+  *out = scale;
+  return WF_OK;
+}
+
+// Dense attention over already validated operands (shared by SDPA and the cache attend when
+// a single split suffices). mask_kind: wf::MASK_*.
+int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const wf_tensor* mask,
+              int mask_kind, bool mask_vec, int causal, float scale, wf_tensor* out, float* lse,
+              int64_t Lk, hipStream_t stream) {
+  const int B = (int)q->shape[0], Hq = (int)q->shape[1], Lq = (int)q->shape[2];
+  const int Dqk = (int)q->shape[3], Hkv = (int)k->shape[1], Dv = (int)v->shape[3];
+  const int G = Hq / Hkv;
+  wf::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q->data; a.q2 = q->data; a.k = k->data; a.k2 = k->data; a.v = v->data;
+  a.o = out->data; a.lse = lse; a.mask = mask ? mask->data : nullptr;
+  a.q_sb = st(q, 0); a.q_sh = st(q, 1); a.q_sm = q->stride[2];
+  a.q2_sb = a.q_sb; a.q2_sh = a.q_sh; a.q2_sm = a.q_sm;
+  a.k_sb = st(k, 0); a.k_sh = st(k, 1); a.k_sm = k->stride[2];
+  a.k2_sb = a.k_sb; a.k2_sh = a.k_sh; a.k2_sm = a.k_sm;
+  a.v_sb = st(v, 0); a.v_sh = st(v, 1); a.v_sm = v->stride[2];
+  a.o_sb = st(out, 0); a.o_sh = st(out, 1); a.o_sm = out->stride[2];
+  if (mask) { a.mk_sb = st(mask, 0); a.mk_sh = st(mask, 1); a.mk_sm = st(mask, 2); }
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.Lq = Lq; a.Lk = (int)Lk;
+  a.causal_shift = 0;
+  a.mask_vec = mask_vec ? 1 : 0;
+  a.scale_log2 = scale * wf::kLog2e;
+  const int dt = kernel_dtype(q->dtype);
+  if (dt == wf::DT_F32) {
+    const wf::F32Entry* e = find_f32(Dqk, Dv, mask_kind, causal);
+    if (!e) return fail(WF_ERR_UNSUPPORTED, "no fp32 kernel for Dqk=%d Dv=%d", Dqk, Dv);
+    a.n_qtiles = (Lq + e->bm - 1) / e->bm;
+    const int64_t blocks = (int64_t)a.n_qtiles * B * Hq;
+    if (blocks > 0x7fffffff) return fail(WF_ERR_SHAPE, "problem too large for one launch");
+    return hip_status(launch(e->fn, dim3((unsigned)blocks), dim3(256), a, stream), "attention launch");
+  }
+  int hpw = 1;
+  if (mask_kind == wf::MASK_NONE) hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const wf::AttnEntry* e = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, mask_kind, causal, wf::MODE_DENSE);
+  if (!e) return fail(WF_ERR_UNSUPPORTED, "no 16-bit kernel for Dqk=%d Dv=%d", Dqk, Dv);
+  a.n_qtiles = (Lq + e->bmp - 1) / e->bmp;
+  const int64_t blocks = (int64_t)a.n_qtiles * B * Hkv * (G / hpw);
+  if (blocks > 0x7fffffff) return fail(WF_ERR_SHAPE, "problem too large for one launch");
+  return hip_status(launch(e->fn, dim3((unsigned)blocks), dim3(e->nw * 64), a, stream),
+                    "attention launch");
+}
+
+int check_cache_state(const wf_block_kv_state* s) {
+  if (s == nullptr) return fail(WF_ERR_NULL, "state is NULL");
+  if (s->chunk <= 0 || s->window <= 0 || s->sink < 0 || s->cache_len <= 0)
+    return fail(WF_ERR_CACHE_CONFIG, "cache sizes must be positive (sink may be 0)");
+  if (s->sink + s->window != s->cache_len)
+    return fail(WF_ERR_CACHE_CONFIG, "sink + window (%lld) must equal the cache length (%lld)",
+                (long long)(s->sink + s->window), (long long)s->cache_len);
+  if (s->cache_len % s->chunk != 0)
+    return fail(WF_ERR_CACHE_CONFIG, "sink + window must be divisible by chunk_size");
+  if (s->window < s->chunk) return fail(WF_ERR_CACHE_CONFIG, "window must hold at least one chunk");
+  if (s->last_chunk < -1) return fail(WF_ERR_CACHE_CONFIG, "corrupt state (last_chunk < -1)");
+  return WF_OK;
+}
+
+void visible_range(const wf_block_kv_state* s, int64_t* T, int64_t* head, int64_t* start,
+                   int64_t* n) {
+  *T = (s->last_chunk + 1) * s->chunk;
+  *head = *T < s->sink ? *T : s->sink;
+  *start = (*T - s->window) > s->sink ? (*T - s->window) : s->sink;
+  *n = *head + (*T > *start ? *T - *start : 0);
+}
+
+constexpr int kMaxSplits = 16;
+
+}  // namespace
+
+extern "C" {
+
+const char* wf_status_string(int status) {
+  switch (status) {
+    case WF_OK: return "WF_OK";
+    case WF_ERR_NULL: return "WF_ERR_NULL";
+    case WF_ERR_SHAPE: return "WF_ERR_SHAPE";
+    case WF_ERR_DTYPE: return "WF_ERR_DTYPE";
+    case WF_ERR_LAYOUT: return "WF_ERR_LAYOUT";
+    case WF_ERR_UNSUPPORTED: return "WF_ERR_UNSUPPORTED";
+    case WF_ERR_CHUNK_ORDER: return "WF_ERR_CHUNK_ORDER";
+    case WF_ERR_CACHE_CONFIG: return "WF_ERR_CACHE_CONFIG";
+    case WF_ERR_WORKSPACE: return "WF_ERR_WORKSPACE";
+    case WF_ERR_HIP: return "WF_ERR_HIP";
+    default: return "WF_ERR_UNKNOWN";
+  }
+}
+
+const char* wf_last_error(void) { return g_last_error.c_str(); }
+
+int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
+                const wf_tensor* mask, int is_causal, float dropout_p, float scale,
+                wf_tensor* out, float* lse, void* stream) {
+  int rc;
+  if ((rc = check_data(q, "q", 4)) || (rc = check_data(k, "k", 4)) ||
+      (rc = check_data(v, "v", 4)) || (rc = check_data(out, "out", 4)))
+    return rc;
+  if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype)
+    return fail(WF_ERR_DTYPE, "q, k, v and out must share one dtype");
+  const int64_t B = q->shape[0], Hq = q->shape[1], Lq = q->shape[2], Dqk = q->shape[3];
+  const int64_t Hkv = k->shape[1], Lk = k->shape[2], Dv = v->shape[3];
+  if (k->shape[0] != B || v->shape[0] != B || k->shape[3] != Dqk || v->shape[1] != Hkv ||
+      v->shape[2] != Lk)
+    return fail(WF_ERR_SHAPE, "k must be [B,Hkv,Lk,Dqk] and v [B,Hkv,Lk,Dv] for q [B,Hq,Lq,Dqk]");
+  if (out->shape[0] != B || out->shape[1] != Hq || out->shape[2] != Lq || out->shape[3] != Dv)
+    return fail(WF_ERR_SHAPE, "out must be [B,Hq,Lq,Dv]");
+  if (Hkv <= 0 || Hq % Hkv != 0)
+    return fail(WF_ERR_SHAPE, "Hq (%lld) must be a positive multiple of Hkv (%lld)",
+                (long long)Hq, (long long)Hkv);
+  if (Lq > 0x7fffffff || Lk > 0x7fffffff || B > 0x7fffffff || Hq > 0x7fffffff)
+    return fail(WF_ERR_SHAPE, "dimension exceeds 2^31");
+  if (dropout_p != 0.f)
+    return fail(WF_ERR_UNSUPPORTED, "dropout_p must be 0 (inference forward only)");
+  if (mask && is_causal)
+    return fail(WF_ERR_UNSUPPORTED, "a mask together with is_causal is not accepted");
+  float sc;
+  if ((rc = resolve_scale(scale, Dqk, &sc))) return rc;
+  const bool f32 = q->dtype == WF_F32;
+  if (f32 ? !((Dqk == 64 || Dqk == 128) && (Dv == 64 || Dv == 96 || Dv == 128))
+          : !((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128)))
+    return fail(WF_ERR_UNSUPPORTED, "head dims Dqk=%lld Dv=%lld are not built for this dtype",
+                (long long)Dqk, (long long)Dv);
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(WF_ERR_LAYOUT, "lse must be 4-byte aligned");
+  int mask_kind = wf::MASK_NONE;
+  bool mask_vec = false;
+  if (mask) {
+    if (mask->ndim != 4) return fail(WF_ERR_SHAPE, "mask must be 4-d [B|1, Hq|1, Lq, Lk]");
+    const int64_t want[4] = {B, Hq, Lq, Lk};
+    for (int i = 0; i < 4; ++i)
+      if (mask->shape[i] != want[i] && !(mask->shape[i] == 1 && i < 2))
+        return fail(WF_ERR_SHAPE, "mask dim %d is %lld, expected %lld%s", i,
+                    (long long)mask->shape[i], (long long)want[i], i < 2 ? " or 1" : "");
+    if (mask->dtype == WF_BOOL) mask_kind = wf::MASK_BOOL;
+    else if (mask->dtype == WF_F32) mask_kind = wf::MASK_F32;
+    else if (mask->dtype == q->dtype && !f32) mask_kind = wf::MASK_HALF;
+    else return fail(WF_ERR_DTYPE, "mask must be bool, f32 or the dtype of q");
+    if (numel(mask) > 0) {
+      if (mask->data == nullptr) return fail(WF_ERR_NULL, "mask->data is NULL");
+      if (Lk > 1 && mask->stride[3] != 1) return fail(WF_ERR_LAYOUT, "mask key stride must be 1");
+      const int ms = esize(mask->dtype);
+      if (reinterpret_cast<uintptr_t>(mask->data) % ms != 0)
+        return fail(WF_ERR_LAYOUT, "mask pointer is not aligned to its element size");
+      mask_vec = reinterpret_cast<uintptr_t>(mask->data) % (4 * ms) == 0;
+      for (int i = 0; i < 3; ++i)
+        if (mask->shape[i] > 1 && mask->stride[i] % 4 != 0) mask_vec = false;
+    }
+  }
+  if (B * Hq * Lq == 0 || Dv == 0) return ok();
+  return run_dense(q, k, v, mask, mask_kind, mask_vec, is_causal ? 1 : 0, sc, out, lse, Lk,
+                   (hipStream_t)stream);
+}
+
+size_t wf_varlen_mla_prefill_workspace_size(int batch, int64_t total_q_tokens, int head_num) {
+  (void)head_num;
+  if (batch < 0 || total_q_tokens < 0) return 0;
+  const int64_t bmp = 256;  // query positions per work item of the built MLA kernel
+  const int64_t max_items = total_q_tokens / bmp + batch;
+  return (size_t)wf::VarlenWs::bytes(batch, max_items);
+}
+
+static int as3d(const wf_tensor* t, const char* name, int64_t heads, wf_tensor* o) {
+  // Accepts [n, H, d] or the flat [n, H*d] form of the same bytes.
+  if (t == nullptr) return fail(WF_ERR_NULL, "%s is NULL", name);
+  *o = *t;
+  if (t->ndim == 2) {
+    if (heads <= 0 || t->shape[1] % heads != 0)
+      return fail(WF_ERR_SHAPE, "%s: flat width %lld is not a multiple of the head count",
+                  name, (long long)t->shape[1]);
+    o->ndim = 3;
+    o->shape[2] = t->shape[1] / heads;
+    o->shape[1] = heads;
+    o->stride[2] = t->stride[1];
+    o->stride[1] = o->shape[2] * t->stride[1];
+  }
+  return check_data(o, name, 3);
+}
+
+int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const wf_tensor* k_,
+                          const wf_tensor* k_rope_, const wf_tensor* v_,
+                          const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
+                          int head_num, int kv_head_num, float qk_scale, int mask_type,
+                          wf_tensor* out_, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc;
+  wf_tensor q, qr, k, kr, v, out;
+  if ((rc = as3d(q_, "q", head_num, &q)) || (rc = as3d(q_rope_, "q_rope", head_num, &qr)) ||
+      (rc = as3d(k_, "k", kv_head_num, &k)) || (rc = as3d(k_rope_, "k_rope", kv_head_num, &kr)) ||
+      (rc = as3d(v_, "v", kv_head_num, &v)) || (rc = as3d(out_, "out", head_num, &out)))
+    return rc;
+  if (q.dtype == WF_F32) return fail(WF_ERR_DTYPE, "MLA prefill takes f16 or bf16");
+  if (qr.dtype != q.dtype || k.dtype != q.dtype || kr.dtype != q.dtype || v.dtype != q.dtype ||
+      out.dtype != q.dtype)
+    return fail(WF_ERR_DTYPE, "all MLA tensors must share one dtype");
+  const int64_t nTq = q.shape[0], nTk = k.shape[0], Dv = q.shape[2];
+  if (head_num <= 0 || kv_head_num <= 0 || head_num % kv_head_num != 0)
+    return fail(WF_ERR_SHAPE, "headNum must be a positive multiple of kvHeadNum");
+  if (q.shape[1] != head_num || qr.shape[1] != head_num || out.shape[1] != head_num ||
+      k.shape[1] != kv_head_num || kr.shape[1] != kv_head_num || v.shape[1] != kv_head_num)
+    return fail(WF_ERR_SHAPE, "head counts disagree with headNum / kvHeadNum");
+  if (qr.shape[0] != nTq || out.shape[0] != nTq || kr.shape[0] != nTk || v.shape[0] != nTk)
+    return fail(WF_ERR_SHAPE, "token counts disagree between q/q_rope/out or k/k_rope/v");
+  if (qr.shape[2] != 64 || kr.shape[2] != 64)
+    return fail(WF_ERR_SHAPE, "the rotary part must be 64 wide");
+  if (k.shape[2] != Dv || v.shape[2] != Dv || out.shape[2] != Dv)
+    return fail(WF_ERR_SHAPE, "q, k, v and out must share the value width");
+  if (Dv != 128) return fail(WF_ERR_UNSUPPORTED, "value width %lld is not built (128)", (long long)Dv);
+  if (mask_type != 0 && mask_type != 1)
+    return fail(WF_ERR_UNSUPPORTED, "mask_type must be 0 (none) or 1 (causal)");
+  if (batch < 0) return fail(WF_ERR_SHAPE, "batch must be >= 0");
+  if (nTq > 0x7fffffff || nTk > 0x7fffffff) return fail(WF_ERR_SHAPE, "token count exceeds 2^31");
+  float sc;
+  if ((rc = resolve_scale(qk_scale, Dv + 64, &sc))) return rc;
+  if (batch > 0 && (q_seqlen == nullptr || kv_seqlen == nullptr))
+    return fail(WF_ERR_NULL, "qSeqLen / kvSeqLen are NULL");
+  const size_t need = wf_varlen_mla_prefill_workspace_size(batch, nTq, head_num);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const wf::AttnEntry* e = find_attn(kernel_dtype(q.dtype), 192, 128, 128, 0, 0, wf::MASK_NONE,
+                                     mask_type, wf::MODE_VARLEN);
+  if (!e) return fail(WF_ERR_UNSUPPORTED, "MLA kernel not built for this dtype");
+  if (batch == 0 || nTq == 0) return ok();
+  if (e->bmp != 256) return fail(WF_ERR_UNSUPPORTED, "internal: MLA tile height changed");
+  const int max_items = (int)(nTq / e->bmp + batch);
+  int* ws = (int*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t he = wf::launch_varlen_schedule(q_seqlen, kv_seqlen, batch, nTq, nTk, e->bmp, e->bn,
+                                             mask_type, max_items, ws, s);
+  if (he != hipSuccess) return hip_status(he, "schedule launch");
+  wf::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q.data; a.q2 = qr.data; a.k = k.data; a.k2 = kr.data; a.v = v.data; a.o = out.data;
+  a.q_sm = q.stride[0]; a.q_sh = q.stride[1];
+  a.q2_sm = qr.stride[0]; a.q2_sh = qr.stride[1];
+  a.k_sm = k.stride[0]; a.k_sh = k.stride[1];
+  a.k2_sm = kr.stride[0]; a.k2_sh = kr.stride[1];
+  a.v_sm = v.stride[0]; a.v_sh = v.stride[1];
+  a.o_sm = out.stride[0]; a.o_sh = out.stride[1];
+  a.B = batch; a.Hq = head_num; a.Hkv = kv_head_num; a.G = head_num / kv_head_num;
+  a.scale_log2 = sc * wf::kLog2e;
+  a.cu_q = (const int*)((char*)workspace + wf::VarlenWs::cu_q_off());
+  a.cu_k = (const int*)((char*)workspace + wf::VarlenWs::cu_k_off(batch));
+  a.items = (const int2*)((char*)workspace + wf::VarlenWs::items_off(batch));
+  a.counter = ws;
+  a.n_items = ws + 1;
+  // The schedule counts (sequence, query tile) items on the device; the kernel expands each
+  // over the head groups and takes work from the counter, so the persistent grid only
+  // needs an upper bound on the work.
+  const int64_t total_work = (int64_t)max_items * (head_num / e->hpw);
+  const int cus = device_cus();
+  const int grid = (int)(total_work < cus ? total_work : cus);
+  return hip_status(launch(e->fn, dim3(grid), dim3(e->nw * 64), a, s), "MLA launch");
+}
+
+int wf_block_kv_init(wf_block_kv_state* s, int64_t cache_len, int64_t sink, int64_t window,
+                     int64_t chunk) {
+  if (s == nullptr) return fail(WF_ERR_NULL, "state is NULL");
+  wf_block_kv_state t;
+  t.cache_len = cache_len; t.sink = sink; t.window = window; t.chunk = chunk; t.last_chunk = -1;
+  int rc = check_cache_state(&t);
+  if (rc) return rc;
+  *s = t;
+  return ok();
+}
+
+int wf_block_kv_cache_update(wf_block_kv_state* s, int64_t chunk_idx, const wf_tensor* k_new,
+                             const wf_tensor* v_new, wf_tensor* k_cache, wf_tensor* v_cache,
+                             void* stream) {
+  int rc;
+  if ((rc = check_cache_state(s))) return rc;
+  if (chunk_idx != s->last_chunk && chunk_idx != s->last_chunk + 1)
+    return fail(WF_ERR_CHUNK_ORDER, "chunk %lld after chunk %lld: only a repeat or the next index",
+                (long long)chunk_idx, (long long)s->last_chunk);
+  if (chunk_idx < 0) return fail(WF_ERR_CHUNK_ORDER, "the first chunk index is 0");
+  bool u16 = true;
+  if ((rc = check_cache_data(k_new, "k_new", &u16)) || (rc = check_cache_data(v_new, "v_new", &u16)) ||
+      (rc = check_cache_data(k_cache, "k_cache", &u16)) ||
+      (rc = check_cache_data(v_cache, "v_cache", &u16)))
+    return rc;
+  if (v_new->dtype != k_new->dtype || k_cache->dtype != k_new->dtype || v_cache->dtype != k_new->dtype)
+    return fail(WF_ERR_DTYPE, "cache and update tensors must share one dtype");
+  const int64_t B = k_cache->shape[0], H = k_cache->shape[1], Dk = k_cache->shape[3];
+  const int64_t Dv = v_cache->shape[3];
+  if (k_cache->shape[2] != s->cache_len || v_cache->shape[2] != s->cache_len ||
+      v_cache->shape[0] != B || v_cache->shape[1] != H)
+    return fail(WF_ERR_SHAPE, "caches must be [B,H,cache_len,D] with cache_len = %lld",
+                (long long)s->cache_len);
+  if (k_new->shape[0] != B || k_new->shape[1] != H || k_new->shape[2] != s->chunk ||
+      k_new->shape[3] != Dk || v_new->shape[0] != B || v_new->shape[1] != H ||
+      v_new->shape[2] != s->chunk || v_new->shape[3] != Dv)
+    return fail(WF_ERR_SHAPE, "updates must be [B,H,chunk,D] with chunk = %lld", (long long)s->chunk);
+  if (B * H > 0 && (Dk > 0 || Dv > 0)) {
+    const int64_t kn[3] = {k_new->stride[0], k_new->stride[1], k_new->stride[2]};
+    const int64_t vn[3] = {v_new->stride[0], v_new->stride[1], v_new->stride[2]};
+    const int64_t kc[3] = {k_cache->stride[0], k_cache->stride[1], k_cache->stride[2]};
+    const int64_t vc[3] = {v_cache->stride[0], v_cache->stride[1], v_cache->stride[2]};
+    hipError_t he = wf::launch_kv_update(u16 ? 16 : esize(k_new->dtype), esize(k_new->dtype), k_new->data, kn, v_new->data, vn,
+                                         k_cache->data, kc, v_cache->data, vc, (int)B, (int)H,
+                                         (int)s->chunk, (int)Dk, (int)Dv, chunk_idx * s->chunk,
+                                         s->sink, s->window, (hipStream_t)stream);
+    if (he != hipSuccess) return hip_status(he, "cache update launch");
+  }
+  s->last_chunk = chunk_idx;
+  return ok();
+}
+
+int wf_block_kv_visible(const wf_block_kv_state* s, int64_t* n_visible, int64_t* phys_index) {
+  int rc;
+  if ((rc = check_cache_state(s))) return rc;
+  if (n_visible == nullptr) return fail(WF_ERR_NULL, "n_visible is NULL");
+  int64_t T, head, start, n;
+  visible_range(s, &T, &head, &start, &n);
+  *n_visible = n;
+  if (phys_index) {
+    for (int64_t p = 0; p < n; ++p) {
+      const int64_t tok = p < head ? p : start + (p - head);
+      phys_index[p] = tok < s->sink ? tok : s->sink + (tok - s->sink) % s->window;
+    }
+  }
+  return ok();
+}
+
+int wf_block_kv_gather(const wf_block_kv_state* s, const wf_tensor* cache, wf_tensor* out,
+                       void* stream) {
+  int rc;
+  if ((rc = check_cache_state(s))) return rc;
+  bool u16 = true;
+  if ((rc = check_cache_data(cache, "cache", &u16)) || (rc = check_cache_data(out, "logical_out", &u16)))
+    return rc;
+  if (out->dtype != cache->dtype) return fail(WF_ERR_DTYPE, "cache and output dtypes differ");
+  int64_t T, head, start, n;
+  visible_range(s, &T, &head, &start, &n);
+  if (cache->shape[2] != s->cache_len) return fail(WF_ERR_SHAPE, "cache length mismatch");
+  if (out->shape[0] != cache->shape[0] || out->shape[1] != cache->shape[1] ||
+      out->shape[2] != n || out->shape[3] != cache->shape[3])
+    return fail(WF_ERR_SHAPE, "logical_out must be [B,H,%lld,D]", (long long)n);
+  const int64_t cs[3] = {cache->stride[0], cache->stride[1], cache->stride[2]};
+  const int64_t os[3] = {out->stride[0], out->stride[1], out->stride[2]};
+  return hip_status(wf::launch_kv_gather(u16 ? 16 : esize(cache->dtype), esize(cache->dtype),
+                                         cache->data, cs, out->data, os,
+                                         (int)cache->shape[0], (int)cache->shape[1], n,
+                                         (int)cache->shape[3], T, s->sink, s->window,
+                                         (hipStream_t)stream),
+                    "gather launch");
+}
+
+size_t wf_block_kv_attend_workspace_size(const wf_block_kv_state* s, int B, int Hq, int Lq,
+                                         int Dv) {
+  if (s == nullptr || B < 0 || Hq < 0 || Lq < 0 || Dv < 0) return 0;
+  const int64_t rows = (int64_t)B * Hq * Lq;
+  return (size_t)(kMaxSplits * rows * ((int64_t)Dv + 1) * 4 + 256);
+}
+
+int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_tensor* k_cache,
+                       const wf_tensor* v_cache, float scale, wf_tensor* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_cache_state(s))) return rc;
+  if ((rc = check_data(q, "q", 4)) || (rc = check_data(k_cache, "k_cache", 4)) ||
+      (rc = check_data(v_cache, "v_cache", 4)) || (rc = check_data(out, "out", 4)))
+    return rc;
+  if (k_cache->dtype != q->dtype || v_cache->dtype != q->dtype || out->dtype != q->dtype)
+    return fail(WF_ERR_DTYPE, "q, caches and out must share one dtype");
+  if (q->dtype == WF_F32) return fail(WF_ERR_DTYPE, "cache attend takes f16 or bf16");
+  const int64_t B = q->shape[0], Hq = q->shape[1], Lq = q->shape[2], D = q->shape[3];
+  const int64_t Hkv = k_cache->shape[1], Dv = v_cache->shape[3];
+  if (k_cache->shape[0] != B || v_cache->shape[0] != B || v_cache->shape[1] != Hkv ||
+      k_cache->shape[2] != s->cache_len || v_cache->shape[2] != s->cache_len || k_cache->shape[3] != D)
+    return fail(WF_ERR_SHAPE, "caches must be [B,Hkv,cache_len,D]");
+  if (out->shape[0] != B || out->shape[1] != Hq || out->shape[2] != Lq || out->shape[3] != Dv)
+    return fail(WF_ERR_SHAPE, "out must be [B,Hq,Lq,Dv]");
+  if (Hkv <= 0 || Hq % Hkv != 0) return fail(WF_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  if (!((D == 64 && Dv == 64) || (D == 128 && Dv == 128)))
+    return fail(WF_ERR_UNSUPPORTED, "head dims (%lld, %lld) not built", (long long)D, (long long)Dv);
+  float sc;
+  if ((rc = resolve_scale(scale, D, &sc))) return rc;
+  const size_t need = wf_block_kv_attend_workspace_size(s, (int)B, (int)Hq, (int)Lq, (int)Dv);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (B * Hq * Lq == 0) return ok();
+  int64_t T, head, start, n_vis;
+  visible_range(s, &T, &head, &start, &n_vis);
+  // Every visible token sits in a slot below n_vis (tokens before the window wraps keep
+  // slot == token; once it wraps every slot is visible), and a non-causal softmax over keys
+  // does not depend on their order, so the kernels read slots [0, n_vis) in place.
+  const int dt = kernel_dtype(q->dtype);
+  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, 4, 1, wf::MASK_NONE, 0, wf::MODE_SPLIT);
+  if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
+  const int n_kt = (int)((n_vis + e->bn - 1) / e->bn);
+  const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
+  const int64_t base_blocks = (int64_t)n_qt * B * Hq;
+  const int cus = device_cus();
+  int n_splits = (int)((2 * cus + base_blocks - 1) / base_blocks);
+  if (n_splits > kMaxSplits) n_splits = kMaxSplits;
+  if (n_splits > n_kt) n_splits = n_kt;
+  if (n_splits <= 1)
+    return run_dense(q, k_cache, v_cache, nullptr, wf::MASK_NONE, false, 0, sc, out, nullptr,
+                     n_vis, (hipStream_t)stream);
+  const int tps = (n_kt + n_splits - 1) / n_splits;
+  n_splits = (n_kt + tps - 1) / tps;
+  wf::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q->data; a.q2 = q->data; a.k = k_cache->data; a.k2 = k_cache->data; a.v = v_cache->data;
+  a.o = out->data;
+  a.q_sb = st(q, 0); a.q_sh = st(q, 1); a.q_sm = q->stride[2];
+  a.q2_sb = a.q_sb; a.q2_sh = a.q_sh; a.q2_sm = a.q_sm;
+  a.k_sb = st(k_cache, 0); a.k_sh = st(k_cache, 1); a.k_sm = k_cache->stride[2];
+  a.k2_sb = a.k_sb; a.k2_sh = a.k_sh; a.k2_sm = a.k_sm;
+  a.v_sb = st(v_cache, 0); a.v_sh = st(v_cache, 1); a.v_sm = v_cache->stride[2];
+  a.B = (int)B; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)(Hq / Hkv); a.Lq = (int)Lq;
+  a.Lk = (int)n_vis;
+  a.n_qtiles = n_qt;
+  a.scale_log2 = sc * wf::kLog2e;
+  a.tiles_per_split = tps;
+  const int64_t rows = B * Hq * Lq;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + (size_t)kMaxSplits * rows * Dv * 4);
+  hipStream_t strm = (hipStream_t)stream;
+  hipError_t he = launch(e->fn, dim3((unsigned)base_blocks, n_splits),
+                         dim3(e->nw * 64), a, strm);
+  if (he != hipSuccess) return hip_status(he, "split attention launch");
+  return hip_status(wf::launch_split_combine(dt, a.part_o, a.part_lse, n_splits, (int)B, (int)Hq,
+                                             (int)Lq, (int)Dv, out->data, st(out, 0), st(out, 1),
+                                             out->stride[2], strm),
+                    "combine launch");
+}
+
+}  // extern "C"

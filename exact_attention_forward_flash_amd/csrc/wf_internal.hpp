@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI layer (wf_api.cpp) and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_fwd.hpp"
+
+namespace wf {
+
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// One compiled instantiation of attn_fwd_kernel.
+struct AttnEntry {
+  int dtype, dqk, dqk1, dv, nw, hpw, mask, causal, mode;
+  const void* fn;   // __global__ void(FwdArgs)
+  int bmp;          // query positions per work group
+  int bn;           // keys per tile
+};
+
+// Tables exported by the kernel translation units.
+const AttnEntry* attn_table_sdpa_bf16_d64(int* n);
+const AttnEntry* attn_table_sdpa_bf16_d128(int* n);
+const AttnEntry* attn_table_sdpa_f16_d64(int* n);
+const AttnEntry* attn_table_sdpa_f16_d128(int* n);
+const AttnEntry* attn_table_mla(int* n);
+const AttnEntry* attn_table_split(int* n);
+
+#define WF_ATTN_ENTRY(T, DT, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE)                     \
+  {DT, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE,                                          \
+   (const void*)&attn_fwd_kernel<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE>,             \
+   AttnFwd<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE>::BMP, 64}
+
+// fp32 path (MFMA 32x32x2 f32).
+struct F32Entry {
+  int dqk, dv, mask, causal;
+  const void* fn;
+  int bm;  // queries per work group
+};
+const F32Entry* attn_table_f32(int* n);
+
+// Auxiliary kernels.
+hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
+                                  int64_t total_q, int64_t total_k, int bmp, int bn, int causal,
+                                  int max_items, int* ws, hipStream_t s);
+hipError_t launch_split_combine(int dtype, const float* part_o, const float* part_lse,
+                                int n_splits, int B, int Hq, int Lq, int Dv, void* out,
+                                int64_t o_sb, int64_t o_sh, int64_t o_sm, hipStream_t s);
+hipError_t launch_kv_update(int unit, int esize, const void* k_new, const int64_t* kn_st,
+                            const void* v_new, const int64_t* vn_st, void* k_cache,
+                            const int64_t* kc_st, void* v_cache, const int64_t* vc_st, int B,
+                            int H, int chunk, int Dk, int Dv, int64_t tok0, int64_t sink,
+                            int64_t window, hipStream_t s);
+hipError_t launch_kv_gather(int unit, int esize, const void* cache, const int64_t* c_st, void* out,
+                            const int64_t* o_st, int B, int H, int64_t n_vis, int D,
+                            int64_t T, int64_t sink, int64_t window, hipStream_t s);
+
+// Varlen workspace layout (bytes from the workspace base).
+struct VarlenWs {
+  static constexpr int64_t kHeaderInts = 64;  // [0] counter, [1] n_items, [2] error
+  __host__ __device__ static int64_t cu_q_off() { return kHeaderInts * 4; }
+  __host__ __device__ static int64_t cu_k_off(int batch) { return cu_q_off() + align(((int64_t)batch + 1) * 4); }
+  __host__ __device__ static int64_t items_off(int batch) { return cu_k_off(batch) + align(((int64_t)batch + 1) * 4); }
+  __host__ __device__ static int64_t bytes(int batch, int64_t max_items) { return items_off(batch) + align(max_items * 8); }
+  __host__ __device__ static int64_t align(int64_t x) { return (x + 255) / 256 * 256; }
+};
+
+}  // namespace wf

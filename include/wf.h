@@ -1,0 +1,189 @@
+/*
+ * wf.h — exact attention forward on AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation is exact scaled-dot-product attention,
+ *     out = softmax(scale * Q K^T + mask) V,
+ * as specified by the pages this library implements:
+ *   [CORE]  WorldFoundry API reference, page "Core 注意力" (core attention):
+ *           section "选择最窄的入口" (choose the narrowest entry point): the PyTorch SDPA
+ *           contract, GQA expansion, exact matmul path; the sentence after the CPU/GPU
+ *           example: a bool mask marks the scores that are kept, a float mask is added
+ *           to the score matrix, dropout must be passed as 0 at inference; section
+ *           "Block KV cache 的调用顺序" (block KV cache call order): chunk protocol and
+ *           the sink + window rule.
+ *   [MLA]   Huawei Ascend CANN ATB page "MLA Prefill": the definition of
+ *           AtbMLAPreFillGetWorkspaceSize / AtbMLAPreFill and its parameter table.
+ *
+ * Conventions for every entry point:
+ *   - All tensor data, sequence-length arrays and workspaces are caller-owned DEVICE
+ *     memory. The library never allocates or frees device memory and never synchronises
+ *     the stream; kernels are enqueued on `stream` (a hipStream_t, NULL = default stream).
+ *   - Arguments are validated completely before anything is enqueued. A call that returns
+ *     an error has enqueued nothing and changed no state. wf_last_error() gives the
+ *     reason (thread-local). Faults inside kernels surface at the caller's next
+ *     synchronisation, as for any asynchronous HIP work.
+ *   - Tensor descriptors hold strides in ELEMENTS. The innermost (head-dim) stride must
+ *     be 1; row/head/batch strides and base pointers must keep every row 16-byte
+ *     aligned (a multiple of 8 elements for 16-bit data, 4 for fp32).
+ *   - Results are deterministic: the same inputs give bit-identical outputs on every run
+ *     (no atomics in any reduction; fixed split and combine order).
+ */
+#ifndef WF_H_
+#define WF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WF_F32 = 0,   /* float32                                   */
+  WF_F16 = 1,   /* IEEE binary16                             */
+  WF_BF16 = 2,  /* bfloat16                                  */
+  WF_BOOL = 3,  /* one byte per element, nonzero = keep      */
+  WF_I32 = 4
+} wf_dtype;
+
+typedef enum {
+  WF_OK = 0,
+  WF_ERR_NULL = 1,         /* a required pointer or descriptor is NULL                 */
+  WF_ERR_SHAPE = 2,        /* shapes disagree with each other or with the operation    */
+  WF_ERR_DTYPE = 3,        /* unsupported or mismatched element type                   */
+  WF_ERR_LAYOUT = 4,       /* inner stride != 1, misaligned pointer or stride          */
+  WF_ERR_UNSUPPORTED = 5,  /* dropout_p != 0, head dim not built, mask with causal ... */
+  WF_ERR_CHUNK_ORDER = 6,  /* block KV cache: chunk index skipped or went backwards    */
+  WF_ERR_CACHE_CONFIG = 7, /* block KV cache: sink/window/chunk sizes break the rule   */
+  WF_ERR_WORKSPACE = 8,    /* workspace NULL, misaligned or smaller than required      */
+  WF_ERR_HIP = 9           /* a HIP launch reported an error                           */
+} wf_status;
+
+/* A strided view of caller-owned device memory. Only the first `ndim` entries of shape
+ * and stride are read. A stride of 0 broadcasts that dimension (masks only). */
+typedef struct {
+  void* data;
+  int32_t dtype;      /* wf_dtype */
+  int32_t ndim;       /* 1..4     */
+  int64_t shape[4];
+  int64_t stride[4];  /* in elements */
+} wf_tensor;
+
+/* ---------------------------------------------------------------------------------------
+ * wf_sdpa_fwd — split-head scaled-dot-product attention forward ([CORE] "选择最窄的入口":
+ * PyTorch SDPA contract with GQA expansion; mask sentence after the CPU/GPU example).
+ *
+ *   q    [B, Hq,  Lq, Dqk]   f32 | f16 | bf16
+ *   k    [B, Hkv, Lk, Dqk]   same dtype as q
+ *   v    [B, Hkv, Lk, Dv ]   same dtype as q
+ *   mask NULL, or 4-d broadcastable to [B, Hq, Lq, Lk] (stride 0 on broadcast dims, key
+ *        stride 1): WF_BOOL = keep where nonzero; a float dtype (q's dtype or WF_F32) is
+ *        added to the scaled score (-inf drops the key).
+ *   is_causal  nonzero: key j is kept for query i iff j <= i (top-left alignment).
+ *              Not accepted together with a mask (WF_ERR_UNSUPPORTED).
+ *   dropout_p  must be 0 (inference); anything else is WF_ERR_UNSUPPORTED.
+ *   scale      multiplies Q K^T; NaN selects 1/sqrt(Dqk). Must be finite and > 0.
+ *   out  [B, Hq, Lq, Dv]     same dtype as q (written; rounding to nearest even)
+ *   lse  NULL, or device float32 [B*Hq*Lq] contiguous: natural-log sum of exp of the
+ *        scaled, masked scores per query (-inf for a query that keeps no key).
+ * GQA: query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of Hkv.
+ * A query that keeps no key gets out = 0.
+ * Built head dims: 16-bit q: (Dqk, Dv) in {(64,64), (128,128)}; fp32: Dqk in {64,128},
+ * Dv in {64, 96, 128}. Others return WF_ERR_UNSUPPORTED.
+ * ------------------------------------------------------------------------------------- */
+int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
+                const wf_tensor* mask, int is_causal, float dropout_p, float scale,
+                wf_tensor* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * MLA prefill over a packed variable-length batch ([MLA] definition and parameter table).
+ *
+ *   q       [nTq, Hq,  Dv]  f16 | bf16 (the value-width "nope" part of the query)
+ *   q_rope  [nTq, Hq,  64]  rotary part of the query (same dtype)
+ *   k       [nTk, Hkv, Dv]  k_rope [nTk, Hkv, 64]   v [nTk, Hkv, Dv]
+ *           A concatenated cache (k_rope stored right after k in each token row) is the
+ *           same call with k_rope->data = k->data + Dv and matching strides.
+ *   q_seqlen, kv_seqlen  device int32 [batch]; sequence i owns query tokens
+ *           [sum_{t<i} q_seqlen[t], ... + q_seqlen[i]) and likewise for keys/values.
+ *   head_num, kv_head_num  Hq, Hkv (Hq a multiple of Hkv; q head h reads kv head
+ *           h / (Hq/Hkv)).
+ *   qk_scale  multiplies (q . k + q_rope . k_rope); finite and > 0.
+ *   mask_type 0 = none (UNDEFINED: an all-zero mask), 1 = causal, aligned bottom-right:
+ *           query i of a sequence keeps key j iff j <= i + kv_len - q_len.
+ *   out     [nTq, Hq, Dv], dtype of q. Rows of queries that keep no key are 0.
+ *   workspace  device memory of at least
+ *           wf_varlen_mla_prefill_workspace_size(batch, nTq, head_num) bytes, 256-byte
+ *           aligned; it holds the tile schedule built on the device from the lengths.
+ * Score width is Dv + 64 with Dv = 128 (the built instantiation).
+ * If the device lengths are negative or sum past nTq / nTk, no attention is computed and
+ * word 2 of the workspace (int32) is set to 1; it is 0 after a good call.
+ * ------------------------------------------------------------------------------------- */
+size_t wf_varlen_mla_prefill_workspace_size(int batch, int64_t total_q_tokens, int head_num);
+int wf_varlen_mla_prefill(const wf_tensor* q, const wf_tensor* q_rope, const wf_tensor* k,
+                          const wf_tensor* k_rope, const wf_tensor* v,
+                          const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
+                          int head_num, int kv_head_num, float qk_scale, int mask_type,
+                          wf_tensor* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Rolling block KV cache ([CORE] "Block KV cache 的调用顺序").
+ *
+ * The cache is two caller-owned device tensors k_cache [B, Hkv, cache_len, Dk] and
+ * v_cache [B, Hkv, cache_len, Dv] plus this caller-owned host state. The first `sink`
+ * tokens are never evicted; the next `window` slots form a ring that holds the newest
+ * tokens. Token t lives in slot t if t < sink, else sink + (t - sink) mod window.
+ * Rules: sink + window == cache_len; cache_len % chunk == 0; window >= chunk.
+ * A snapshot of the cache is a copy of the state and the two tensors.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  int64_t cache_len, sink, window, chunk;
+  int64_t last_chunk; /* -1 while empty */
+} wf_block_kv_state;
+
+int wf_block_kv_init(wf_block_kv_state* st, int64_t cache_len, int64_t sink, int64_t window,
+                     int64_t chunk);
+
+/* before_update(chunk_idx) + update(k_new, v_new) + after_update(chunk_idx) in one call:
+ * chunk_idx must equal last_chunk (overwrite the same logical chunk) or last_chunk + 1
+ * (append / roll); anything else is WF_ERR_CHUNK_ORDER with nothing changed.
+ *   k_new [B, Hkv, chunk, Dk], v_new [B, Hkv, chunk, Dv], same dtype as the caches
+ *   (f32 | f16 | bf16). The copy is enqueued on `stream`; st->last_chunk is updated on
+ *   success. */
+int wf_block_kv_cache_update(wf_block_kv_state* st, int64_t chunk_idx,
+                             const wf_tensor* k_new, const wf_tensor* v_new,
+                             wf_tensor* k_cache, wf_tensor* v_cache, void* stream);
+
+/* Number of visible tokens (sink prefix plus the window, including the newest chunk) and,
+ * if phys_index is not NULL, the cache slot of each visible token in chronological order
+ * (host array of n_visible entries). Host-only; enqueues nothing. */
+int wf_block_kv_visible(const wf_block_kv_state* st, int64_t* n_visible,
+                        int64_t* phys_index);
+
+/* Writes the visible tokens of `cache` [B, H, cache_len, D] in chronological order into
+ * logical_out [B, H, n_visible, D] (same dtype), using the same slot map as the attend
+ * kernel. A test aid for checking the cache bit-exactly. */
+int wf_block_kv_gather(const wf_block_kv_state* st, const wf_tensor* cache,
+                       wf_tensor* logical_out, void* stream);
+
+/* Attention of the current chunk's queries over every visible cached token (including
+ * the chunk itself), non-causal.
+ *   q [B, Hq, Lq, Dk] (Hq a multiple of Hkv), out [B, Hq, Lq, Dv]; 16-bit dtypes with
+ *   (Dk, Dv) in {(64,64), (128,128)}. scale as in wf_sdpa_fwd.
+ *   workspace: at least wf_block_kv_attend_workspace_size(...) bytes, 256-byte aligned;
+ *   it holds per-split partial results (fp32) that a combine kernel merges. */
+size_t wf_block_kv_attend_workspace_size(const wf_block_kv_state* st, int B, int Hq, int Lq,
+                                         int Dv);
+int wf_block_kv_attend(const wf_block_kv_state* st, const wf_tensor* q,
+                       const wf_tensor* k_cache, const wf_tensor* v_cache, float scale,
+                       wf_tensor* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Human-readable status name, and the thread-local detail of the last failed call. */
+const char* wf_status_string(int status);
+const char* wf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WF_H_ */

@@ -50,7 +50,8 @@ def _f64(x):
         if x.dtype.is_floating_point:
             x = x.double()
         return x.numpy()
-    return np.asarray(x)
+    x = np.asarray(x)
+    return x.astype(np.float64) if np.issubdtype(x.dtype, np.floating) else x
 
 
 def _softmax_rows(s, vg):

@@ -1,0 +1,113 @@
+"""GPU checks of the rolling block KV cache: contents and indices bit-exact against the
+oracle's token list, and the attend within tolerance of the oracle's SDPA on that view."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_forward_flash_amd import BlockKVCache, ChunkOrderError
+from synth import cache_stream_chunks
+from tests.parity import assert_close, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_page_example_on_gpu():
+    gold = json.load(open(os.path.join(GOLDEN, "block_kv_cache_example.json")))
+    c = BlockKVCache(gold["k_shape"], gold["v_shape"], gold["seq_dim"], gold["chunk_size"],
+                     gold["window_size"], gold["sink_size"], device=DEV, dtype=torch.float32)
+    for idx in range(gold["chunks"]):
+        k = torch.full((1, 1, 2, 2), float(idx), device=DEV)
+        v = torch.full((1, 1, 2, 3), float(idx), device=DEV)
+        c.before_update(idx)
+        c.update(k, v)
+        vk, vv = c.cached_k().cpu(), c.cached_v().cpu()
+        c.after_update(idx)
+        assert vk.shape[2] == gold["expected_visible_counts"][idx]
+        assert vk[0, 0, :, 0].tolist() == gold["expected_visible_values"][idx]
+        assert torch.equal(vv[0, 0, :, :], vk[0, 0, :, :1].expand(-1, 3))
+
+
+@pytest.mark.parametrize("sink,window,chunk,dtype,seq_dim", [
+    (2, 6, 2, torch.float16, 2), (0, 8, 4, torch.bfloat16, 2), (5, 3, 2, torch.float16, 2),
+    (4, 12, 4, torch.float32, 1), (3, 9, 3, torch.bfloat16, 1)])
+def test_random_walk_bit_exact(sink, window, chunk, dtype, seq_dim):
+    L, H, D = sink + window, 2, 64
+    shape = (1, H, L, D) if seq_dim == 2 else (1, L, H, D)
+    c = BlockKVCache(shape, shape, seq_dim, chunk, window, sink, device=DEV, dtype=dtype)
+    o = oracle.BlockKVCacheOracle(shape, shape, seq_dim, chunk, window, sink)
+    g = torch.Generator().manual_seed(L * 10 + chunk)
+    rng = np.random.default_rng(L)
+    idx = 0
+    cshape = (1, H, chunk, D) if seq_dim == 2 else (1, chunk, H, D)
+    for step in range(14):
+        k = torch.randn(cshape, generator=g).to(dtype)
+        v = torch.randn(cshape, generator=g).to(dtype)
+        o.update(idx, k.numpy() if dtype != torch.bfloat16 else k.float().numpy(),
+                 v.numpy() if dtype != torch.bfloat16 else v.float().numpy())
+        c.before_update(idx)
+        c.update(k.to(DEV), v.to(DEV))
+        assert np.array_equal(c.cached_k().cpu().float().numpy(), o.cached_k().astype(np.float32))
+        assert np.array_equal(c.cached_v().cpu().float().numpy(), o.cached_v().astype(np.float32))
+        c.after_update(idx)
+        idx = idx + 1 if rng.random() < 0.7 else idx
+    with pytest.raises(ChunkOrderError):
+        c.before_update(idx + 2)
+        c.update(torch.zeros(cshape, dtype=dtype, device=DEV), torch.zeros(cshape, dtype=dtype, device=DEV))
+
+
+def _attend_check(c, o, q, what):
+    out = c.attend(q.to(DEV))
+    kv, vv = o.cached_k(), o.cached_v()
+    ref, _ = oracle.sdpa(q, torch.from_numpy(kv), torch.from_numpy(vv),
+                         scale=np.float32(1.0 / np.sqrt(q.shape[-1])))
+    assert_close(out, ref, q.dtype, what)
+
+
+@pytest.mark.parametrize("heads,check_chunks", [(4, {0, 1, 14, 15, 16, 17, 40, 63}), (24, {16, 63})])
+def test_cache_stream(heads, check_chunks):
+    """fp16, d=128, chunk 256, sink 256 + window 3840, 64 chunks; per chunk: update, then the
+    chunk's 256 queries attend (non-causally) to every visible token including themselves."""
+    shape = (1, heads, 4096, 128)
+    c = BlockKVCache(shape, shape, 2, 256, 3840, 256, device=DEV, dtype=torch.float16)
+    o = oracle.BlockKVCacheOracle(shape, shape, 2, 256, 3840, 256)
+    for idx, q, k, v in cache_stream_chunks(H=24):
+        q, k, v = q[:, :heads], k[:, :heads], v[:, :heads]
+        c.before_update(idx)
+        c.update(k.to(DEV), v.to(DEV))
+        o.update(idx, k.numpy(), v.numpy())
+        if idx in check_chunks:
+            n, _ = c.visible()
+            assert n == min((idx + 1) * 256, 4096)
+            assert np.array_equal(c.cached_k().cpu().numpy(), o.cached_k())
+            _attend_check(c, o, q, f"chunk {idx}")
+        else:
+            c.attend(q.to(DEV))
+        c.after_update(idx)
+
+
+def test_attend_small_split_and_dense_paths():
+    """Few visible tokens take the single-split path; many take split-KV plus the combine."""
+    for sink, window, chunk, steps in ((0, 64, 64, 1), (64, 448, 64, 12)):
+        shape = (1, 2, sink + window, 64)
+        c = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=torch.bfloat16)
+        o = oracle.BlockKVCacheOracle(shape, shape, 2, chunk, window, sink)
+        g = torch.Generator().manual_seed(steps)
+        for idx in range(steps):
+            k = torch.randn(1, 2, chunk, 64, generator=g).to(torch.bfloat16)
+            v = torch.randn(1, 2, chunk, 64, generator=g).to(torch.bfloat16)
+            q = torch.randn(1, 4, 100, 64, generator=g).to(torch.bfloat16)  # GQA: 4 q heads
+            c.before_update(idx)
+            c.update(k.to(DEV), v.to(DEV))
+            o.update(idx, k.float().numpy(), v.float().numpy())
+            kv = torch.from_numpy(o.cached_k()).to(torch.bfloat16)
+            vv = torch.from_numpy(o.cached_v()).to(torch.bfloat16)
+            out = c.attend(q.to(DEV))
+            ref, _ = oracle.sdpa(q, kv, vv, scale=np.float32(1.0 / 8.0))
+            assert_close(out, ref, torch.bfloat16, f"step {idx}")
+            c.after_update(idx)

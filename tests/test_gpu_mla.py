@@ -1,0 +1,116 @@
+"""GPU parity of wf_varlen_mla_prefill (packed varlen, 128 + 64 score split) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_forward_flash_amd import varlen_mla_prefill, varlen_mla_prefill_workspace_size
+from synth import varlen_mla_prefill_inputs
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu(w, **kw):
+    t = {n: w[n].to(DEV) for n in ("q", "q_rope", "k", "k_rope", "v", "q_seqlen", "kv_seqlen")}
+    return varlen_mla_prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], t["q_seqlen"],
+                              t["kv_seqlen"], w["head_num"], w["kv_head_num"], w["qk_scale"],
+                              w["mask_type"], **kw)
+
+
+def _inputs(qlens, kvlens, H, Hkv, dtype="bf16", seed=1, mask_type=1):
+    g = torch.Generator().manual_seed(seed)
+    nq, nk = sum(qlens), sum(kvlens)
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    r = lambda *s: torch.randn(*s, generator=g).to(dt)
+    return {"q": r(nq, H, 128), "q_rope": r(nq, H, 64), "k": r(nk, Hkv, 128),
+            "k_rope": r(nk, Hkv, 64), "v": r(nk, Hkv, 128),
+            "q_seqlen": torch.tensor(qlens, dtype=torch.int32),
+            "kv_seqlen": torch.tensor(kvlens, dtype=torch.int32),
+            "head_num": H, "kv_head_num": Hkv, "qk_scale": 1.0 / np.sqrt(192.0),
+            "mask_type": mask_type}
+
+
+def _oracle(w):
+    return oracle.varlen_mla_prefill(w["q"], w["q_rope"], w["k"], w["k_rope"], w["v"],
+                                     w["q_seqlen"], w["kv_seqlen"], w["head_num"],
+                                     w["kv_head_num"], np.float32(w["qk_scale"]), w["mask_type"])
+
+
+CASES = [  # q lengths, kv lengths, H, Hkv, dtype, mask_type
+    ([1, 63, 64, 65, 300, 0, 777], None, 4, 4, "bf16", 1),
+    ([1, 63, 64, 65, 300, 0, 777], None, 4, 4, "bf16", 0),
+    ([200, 31, 513], [260, 31, 600], 4, 2, "bf16", 1),   # cached prefix: kv_len > q_len
+    ([257, 1000], None, 2, 1, "fp16", 1),
+    ([90, 5], [40, 5], 2, 2, "fp16", 1),                  # kv_len < q_len: early rows see nothing
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_varlen_small(case):
+    qlens, kvlens, H, Hkv, dt, mt = case
+    w = _inputs(qlens, kvlens or qlens, H, Hkv, dt, mask_type=mt)
+    out = _gpu(w)
+    assert_close(out, _oracle(w), w["q"].dtype, str(case))
+
+
+def test_flat_layout_and_concatenated_cache():
+    w = _inputs([100, 300], [100, 300], 4, 4, "bf16", seed=4)
+    ref = _gpu(w)
+    t = {n: w[n].to(DEV) for n in ("q", "q_rope", "k", "k_rope", "v", "q_seqlen", "kv_seqlen")}
+    kcat = torch.cat([t["k"], t["k_rope"]], dim=-1)          # [nTk, Hkv, 192]: nope then rope
+    out = varlen_mla_prefill(t["q"].reshape(400, -1), t["q_rope"].reshape(400, -1), kcat[..., :128],
+                             kcat[..., 128:], t["v"], t["q_seqlen"], t["kv_seqlen"], 4, 4,
+                             w["qk_scale"], 1)
+    assert torch.equal(out, ref)
+
+
+def test_bad_lengths_set_the_error_word_and_compute_nothing():
+    w = _inputs([100, 300], [100, 300], 2, 2, "bf16", seed=5)
+    t = {n: w[n].to(DEV) for n in ("q", "q_rope", "k", "k_rope", "v")}
+    bad = torch.tensor([100, 301], dtype=torch.int32, device=DEV)    # sums past nTq
+    ws = torch.zeros(varlen_mla_prefill_workspace_size(2, 400, 2), dtype=torch.uint8, device=DEV)
+    from exact_attention_forward_flash_amd import api
+    out = varlen_mla_prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], bad, bad, 2, 2,
+                             w["qk_scale"], 1, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[2]) == 1
+    neg = torch.tensor([100, -1], dtype=torch.int32, device=DEV)
+    varlen_mla_prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], neg, neg, 2, 2,
+                       w["qk_scale"], 1, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[2]) == 1
+    good = t["q"].new_tensor([100, 300], dtype=torch.int32)
+    varlen_mla_prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], good, good, 2, 2,
+                       w["qk_scale"], 1, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[2]) == 0
+
+
+def test_deterministic():
+    w = _inputs([700, 50, 1300], [700, 50, 1300], 4, 4, "bf16", seed=6)
+    assert torch.equal(_gpu(w), _gpu(w))
+
+
+def test_varlen_mla_full_size_sampled():
+    """16 sequences with lengths uniform in [128, 8192] (seed 7), 16 heads, 128 + 64 score
+    split, causal; rows sampled from the shortest, longest and a middle sequence."""
+    w = varlen_mla_prefill_inputs()
+    out = _gpu(w).cpu()
+    assert torch.isfinite(out).all()
+    lens = w["q_seqlen"].tolist()
+    cu = oracle.cu_seqlens(lens)
+    order = np.argsort(lens)
+    for si in (order[0], order[len(order) // 2], order[-1]):
+        L, base = lens[si], cu[si]
+        for h in (0, 11):
+            for i0, i1 in ((0, 32), (L // 2, L // 2 + 32), (L - 32, L)):
+                i1 = min(i1, L)
+                rows = slice(base + i0, base + i1)
+                keys = slice(base, base + i1)
+                ref = oracle.varlen_mla_prefill(
+                    w["q"][rows, h:h + 1], w["q_rope"][rows, h:h + 1], w["k"][keys, h:h + 1],
+                    w["k_rope"][keys, h:h + 1], w["v"][keys, h:h + 1], [i1 - i0], [i1], 1, 1,
+                    np.float32(w["qk_scale"]), 1)
+                assert_close(out[rows, h:h + 1], ref, torch.bfloat16, f"seq {si} head {h} rows {i0}:{i1}")

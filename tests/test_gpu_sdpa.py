@@ -1,0 +1,164 @@
+"""GPU parity of wf_sdpa_fwd against the fp64 oracle (through the C ABI via the binding)."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_forward_flash_amd import sdpa, WfError
+from synth import causal_gqa_prefill, masked_sdpa_inputs, page_example_fp32, random_sdpa_inputs
+from tests.parity import assert_close, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run(w, **kw):
+    q, k, v = (w[n].to(DEV) for n in ("q", "k", "v"))
+    m = w.get("mask")
+    return sdpa(q, k, v, attn_mask=None if m is None else m.to(DEV), scale=w["scale"], **kw)
+
+
+def test_page_example_fp32():
+    w = page_example_fp32()
+    out = run(w)
+    assert tuple(out.shape) == (2, 8, 32, 96)
+    ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], scale=np.float32(w["scale"]))
+    assert_close(out, ref, torch.float32, "page example")
+
+
+CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, causal
+    ("bf16", 1, 1, 1, 1, 1, 128, False),
+    ("bf16", 2, 4, 4, 37, 300, 128, False),
+    ("bf16", 2, 8, 2, 256, 256, 128, True),
+    ("bf16", 1, 8, 2, 300, 129, 128, False),
+    ("bf16", 1, 4, 1, 513, 700, 128, True),
+    ("bf16", 2, 4, 2, 700, 513, 64, True),
+    ("fp16", 2, 6, 3, 129, 1000, 64, False),
+    ("fp16", 1, 8, 8, 1024, 1024, 128, True),
+    ("fp16", 3, 2, 1, 77, 77, 64, True),
+    ("bf16", 1, 16, 4, 96, 2049, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_random_shapes(case):
+    dt, B, Hq, Hkv, Lq, Lk, D, causal = case
+    w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 1000)
+    out, lse = run(w, is_causal=causal, return_lse=True)
+    ref, ref_lse = oracle.sdpa(w["q"], w["k"], w["v"], is_causal=causal, scale=np.float32(w["scale"]))
+    assert_close(out, ref, w["q"].dtype, str(case))
+    live = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(to64(lse)), live)
+    assert np.abs(to64(lse)[live] - ref_lse[live]).max() < 1e-3
+
+
+F32_CASES = [(2, 4, 2, 33, 50, 64, 96, False), (1, 4, 4, 130, 70, 128, 128, True),
+             (2, 2, 1, 64, 64, 64, 64, True), (1, 2, 2, 5, 300, 128, 64, False)]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[str(c) for c in F32_CASES])
+def test_fp32_shapes(case):
+    B, Hq, Hkv, Lq, Lk, Dqk, Dv, causal = case
+    w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, Dqk, Dv, "fp32", seed=3)
+    out = run(w, is_causal=causal)
+    ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], is_causal=causal, scale=np.float32(w["scale"]))
+    assert_close(out, ref, torch.float32, str(case))
+
+
+MASK_CASES = [  # dtype, mask kind, mask broadcast shape, Lq, Lk, D
+    ("fp16", "bool", "b1", 200, 320, 64),
+    ("bf16", "bool", "11", 64, 301, 128),     # Lk % 4 != 0: element-wise mask loads
+    ("fp16", "bool", "bh", 130, 256, 64),
+    ("fp16", "half", "b1", 256, 200, 64),
+    ("bf16", "half", "bh", 90, 333, 128),
+    ("bf16", "f32", "11", 128, 128, 128),
+    ("fp32", "bool", "b1", 70, 90, 64),
+    ("fp32", "f32", "bh", 33, 130, 128),
+]
+
+
+def _mask(kind, bshape, B, H, Lq, Lk, dtype, g):
+    shp = {"b1": (B, 1, Lq, Lk), "11": (1, 1, Lq, Lk), "bh": (B, H, Lq, Lk)}[bshape]
+    keep = torch.rand(shp, generator=g) < 0.8
+    keep[..., 0] = True
+    if kind == "bool":
+        return keep
+    vals = torch.randn(shp, generator=g).masked_fill(~keep, float("-inf"))
+    return vals.to(torch.float32 if kind == "f32" else dtype)
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[str(c) for c in MASK_CASES])
+def test_masks(case):
+    dt, kind, bshape, Lq, Lk, D = case
+    B, H = 2, 4
+    w = random_sdpa_inputs(B, H, H, Lq, Lk, D, D, dt, seed=11)
+    g = torch.Generator().manual_seed(12)
+    w["mask"] = _mask(kind, bshape, B, H, Lq, Lk, w["q"].dtype, g)
+    out = run(w)
+    ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w["mask"], scale=np.float32(w["scale"]))
+    assert_close(out, ref, w["q"].dtype, str(case))
+
+
+def test_fully_masked_rows_and_empty_keys():
+    w = random_sdpa_inputs(1, 2, 2, 40, 70, 64, 64, "bf16", seed=5)
+    m = torch.ones(1, 1, 40, 70, dtype=torch.bool)
+    m[0, 0, 7] = False
+    m[0, 0, 33] = False
+    w["mask"] = m
+    out, lse = run(w, return_lse=True)
+    o = to64(out)
+    assert np.all(o[:, :, 7] == 0) and np.all(o[:, :, 33] == 0)
+    assert np.all(np.isneginf(to64(lse)[:, :, [7, 33]]))
+    ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=m, scale=np.float32(w["scale"]))
+    assert_close(out, ref, torch.bfloat16, "fully masked rows")
+    w0 = random_sdpa_inputs(1, 2, 2, 40, 0, 64, 64, "bf16", seed=6)
+    out0 = run(w0)
+    assert out0.shape == (1, 2, 40, 64) and torch.all(out0 == 0)
+
+
+def test_deterministic():
+    w = random_sdpa_inputs(2, 8, 2, 300, 500, 128, 128, "bf16", seed=9)
+    a = run(w, is_causal=True)
+    b = run(w, is_causal=True)
+    assert torch.equal(a, b)
+
+
+def test_errors_surface_as_exceptions():
+    w = random_sdpa_inputs(1, 2, 2, 8, 8, 64, 64, "bf16")
+    with pytest.raises(WfError):
+        run(w, dropout_p=0.1)
+
+
+def _sampled_rows_causal(w, out, picks, rows):
+    """Rows [i0, i1) of a causal problem: q rows i0..i1-1 against keys 0..i1-1, bottom-right."""
+    q, k, v = w["q"], w["k"], w["v"]
+    G = q.shape[1] // k.shape[1]
+    for b, h in picks:
+        for i0, i1 in rows:
+            ref, _ = oracle.sdpa(q[b:b + 1, h:h + 1, i0:i1], k[b:b + 1, h // G:h // G + 1, :i1],
+                                 v[b:b + 1, h // G:h // G + 1, :i1], is_causal=True,
+                                 scale=np.float32(w["scale"]), causal_align="bottom_right")
+            assert_close(out[b:b + 1, h:h + 1, i0:i1], ref, q.dtype, f"b{b} h{h} rows {i0}:{i1}")
+
+
+def test_causal_gqa_prefill_full_size_sampled():
+    """B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal, in the benchmark's launch configuration;
+    sampled rows across the sequence checked against the oracle."""
+    w = causal_gqa_prefill()
+    out = run(w, is_causal=True)
+    assert tuple(out.shape) == (4, 32, 4096, 128)
+    assert torch.isfinite(out).all()
+    _sampled_rows_causal(w, out.cpu(), [(0, 0), (1, 5), (2, 17), (3, 31)],
+                         [(0, 64), (1000, 1040), (2047, 2113), (4032, 4096)])
+
+
+@pytest.mark.parametrize("kind", ["bool", "float"])
+def test_masked_sdpa_full_size(kind):
+    """B=2, H=16, L=2048, d=64 fp16 with a [2,1,L,L] mask broadcast over heads, fully checked."""
+    w = masked_sdpa_inputs(kind)
+    out = run(w)
+    ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w["mask"], scale=np.float32(w["scale"]))
+    assert_close(out, ref, torch.float16, f"masked {kind}")
