@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 3 times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the attention path here has no multi-GPU mode "
@@ -96,6 +99,16 @@ def main():
     import torch
     import exact_attention_forward_flash_amd as wf
     from synth import causal_gqa_prefill
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n}), flush=True)
+        return
 
     if not os.path.exists(wf._lib.LIB_PATH):
         from exact_attention_forward_flash_amd.build import build

@@ -27,6 +27,8 @@
 //   K tile row r (a key), chunk c (8 head-dim elements) at chunk position c ^ (r % 8).
 //   V tile row r, chunk c at position c ^ (2 * (r % 4)).
 #pragma once
+#include <type_traits>
+
 #include "wf_device.hpp"
 
 namespace wf {
@@ -48,6 +50,7 @@ struct FwdArgs {
   int n_qtiles;       // query tiles per head group (dense / split)
   int mask_vec;       // mask rows allow 4-element vector loads
   float scale_log2;   // scale * log2(e)
+  float inv_scale;    // 1 / scale (float masks are added to raw scores as mask / scale)
   // varlen (persistent) mode
   const int* cu_q; const int* cu_k; const int2* items; int* counter; const int* n_items;
   // split-KV mode
@@ -79,6 +82,18 @@ struct AttnFwd {
   static_assert(NW % HPW == 0, "waves split evenly over heads");
   static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile copies split evenly");
   static_assert(KCH % 8 == 0 && VCH % 8 == 0 && DQK1 % 16 == 0 && DV % 32 == 0, "tile shape");
+
+  // LDS swizzles (chunk position = chunk ^ swizzle(row)). They keep the MFMA operand reads
+  // conflict-free whether the LDS serves 128 or 256 bytes per clock:
+  //  K (16-byte reads, lane -> row): any 8 and any 16 consecutive rows get distinct banks.
+  //  V (8-byte transpose reads over 4 consecutive rows x 2 or 4 chunks): the 4 rows of a
+  //    16-lane group and of a 32-lane group land on distinct banks.
+  static __device__ __forceinline__ int kswz(int row) {
+    return KCH == 16 ? (row & 15) : ((row ^ ((row >> 3) & 3)) & 7);  // period 32 in row
+  }
+  static __device__ __forceinline__ int vswz(int row) {
+    return VCH == 16 ? (((row & 1) * 6) ^ ((row & 2) * 5)) : 2 * (row & 3);
+  }
 
   // Number of key tiles a work group covering positions [pos0, pos0 + BMP) must visit.
   static __device__ __forceinline__ int tile_end(int pos0, int Lk, int shift) {
@@ -131,7 +146,7 @@ struct AttnFwd {
     for (int i = 0; i < KLOADS; ++i) {
       const int p = (i * NW + w) * 64 + lane;
       const int r = p / KCH, pos = p % KCH;
-      const int col = (pos ^ (r & 7)) * 8;
+      const int col = (pos ^ kswz(r)) * 8;
       krow[i] = r;
       if (DQK1 == DQK || col < DQK1) { ksrc[i] = kp + col; kstride[i] = a.k_sm; }
       else { ksrc[i] = k2p + (col - DQK1); kstride[i] = a.k2_sm; }
@@ -143,12 +158,12 @@ struct AttnFwd {
       const int p = (i * NW + w) * 64 + lane;
       const int r = p / VCH, pos = p % VCH;
       vrow[i] = r;
-      vsrc[i] = vp + ((pos ^ (2 * (r & 3))) * 8);
+      vsrc[i] = vp + ((pos ^ vswz(r)) * 8);
     }
     const int lk_last = it.Lk - 1;
     // Rows past the last key are clamped onto it: their scores are masked to -inf, and
     // the duplicated V rows meet p = 0.
-    auto issue = [&](int kt, WF_LDS char* Kt, WF_LDS char* Vt) {
+    auto issue_k = [&](int kt, WF_LDS char* Kt) {
       const int k0 = kt * BN;
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i) {
@@ -156,6 +171,9 @@ struct AttnFwd {
         r = r < lk_last ? r : lk_last;
         dma16(ksrc[i] + (int64_t)r * kstride[i], Kt + (i * NW + w) * 1024);
       }
+    };
+    auto issue_v = [&](int kt, WF_LDS char* Vt) {
+      const int k0 = kt * BN;
 #pragma unroll
       for (int i = 0; i < VLOADS; ++i) {
         int r = k0 + vrow[i];
@@ -165,20 +183,22 @@ struct AttnFwd {
     };
 
     // ---- LDS operand offsets ----------------------------------------------------------
-    // K operand (A of S^T): lane (j, hf) reads key row 32kb + j, chunk 2s + hf.
-    int koff[4];
+    // K operand (A of S^T): lane (j, hf) reads key row 32kb + j, chunk 2s + hf
+    // (swizzle(32kb + j) == swizzle(j)).
+    int koff[NS];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) koff[s4] = j * KCH * 16 + (((2 * s4 + hf) ^ (j & 7)) * 16);
+    for (int s = 0; s < NS; ++s) koff[s] = j * KCH * 16 + (((2 * s + hf) ^ kswz(j)) * 16);
     // V^T operand (A of O^T) through the transpose read: within each 16-lane group, lane
     // s names row kbase + s/4, head-dim columns dbase + 4*(s%4) .. +3, so lane t receives
     // head-dim dbase + t for the 4 keys kbase .. kbase+3. kbase = 16m + 4hf (+8 for the
     // second read), dbase = 32n + 16*((lane/16)%2).
-    const int g16 = (lane >> 4) & 1, b2 = (lane & 3) >> 1, fv = 2 * ((lane & 15) >> 2);
-    int voff[2];
+    const int g16 = (lane >> 4) & 1, b2 = (lane & 3) >> 1;
+    const int vrow0 = 4 * hf + ((lane & 15) >> 2);  // row within each 16-key step (+16m, +8)
+    const int fv = vswz(vrow0);                      // rows 16m + vrow0 (+8) share it
+    int voff[NDV];
 #pragma unroll
-    for (int n2 = 0; n2 < 2; ++n2)
-      voff[n2] = (4 * hf + ((lane & 15) >> 2)) * VCH * 16 +
-                 (((4 * n2 + 2 * g16 + b2) ^ fv) * 16) + 8 * (lane & 1);
+    for (int n = 0; n < NDV; ++n)
+      voff[n] = vrow0 * VCH * 16 + (((4 * n + 2 * g16 + b2) ^ fv) * 16) + 8 * (lane & 1);
 
     // ---- mask row ---------------------------------------------------------------------
     const char* mrow = nullptr;
@@ -195,13 +215,37 @@ struct AttnFwd {
       for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    auto compute = [&](int kt, const WF_LDS char* Kt, const WF_LDS char* Vt) {
-      const int k0 = kt * BN;
-      if (CAUSAL && k0 > qlo + 31 + it.shift) return;  // every query of this wave is done
-      const bool need_mask = MASK != MASK_NONE || (k0 + BN > it.Lk) ||
-                             (CAUSAL && k0 + BN - 1 > qlo + it.shift);
+    // Tiles this wave computes: [kt_lo, kt_live). With causal masking a wave is done once a
+    // tile starts past its last query; it still copies tiles and meets the barriers.
+    int kt_live = it.kt_hi;
+    if (CAUSAL) {
+      const int lim = qlo + 31 + it.shift;
+      const int e = lim < 0 ? 0 : lim / BN + 1;
+      kt_live = e < kt_live ? e : kt_live;
+    }
+    if (kt_live < it.kt_lo) kt_live = it.kt_lo;
 
-      // Mask terms (log2 units) for this lane's keys k0 + 32kb + 8q4 + 4hf + e.
+    // ---- operand fragments from LDS ----------------------------------------------------
+    auto kfrag = [&](const WF_LDS char* Kt, int s, int kb) {
+      return lds_read16(Kt + koff[s] + kb * 32 * KCH * 16);
+    };
+    auto vfrag = [&](const WF_LDS char* Vt, int m, int n) {
+      const WF_LDS char* base = Vt + voff[n] + 16 * m * VCH * 16;
+      const u32x2 lo = lds_read_tr(base);
+      const u32x2 hi = lds_read_tr(base + 8 * VCH * 16);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+
+    // ---- masking in the raw score domain ---------------------------------------------------
+    // Element r of block kb is key k0 + 32kb + 8(r/4) + 4hf + r%4. Dropped keys become -inf;
+    // a float mask m is added as m / scale so that scale*log2(e) times the stored value is
+    // the log2-domain score plus log2(e) m.
+    auto need_mask = [&](int kt) {
+      const int k0 = kt * BN;
+      return MASK != MASK_NONE || (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > qlo + it.shift);
+    };
+    auto apply_mask = [&](int kt, f32x16* sc) {
+      const int k0 = kt * BN;
       float mval[2][4][4];
       if constexpr (MASK != MASK_NONE) {
         const bool vec = a.mask_vec && (k0 + BN <= it.Lk);
@@ -220,11 +264,11 @@ struct AttnFwd {
                 typedef T t4 __attribute__((ext_vector_type(4)));
                 const t4 hv = *reinterpret_cast<const t4*>(mrow + 2 * key);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = (float)hv[e] * kLog2e;
+                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = (float)hv[e];
               } else {
                 const f32x4 f4 = *reinterpret_cast<const f32x4*>(mrow + 4 * key);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = f4[e] * kLog2e;
+                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = f4[e];
               }
             } else {
 #pragma unroll
@@ -233,54 +277,57 @@ struct AttnFwd {
                 float mv = -INFINITY;
                 if (kk < it.Lk) {
                   if constexpr (MASK == MASK_BOOL) mv = mrow[kk] ? 0.f : -INFINITY;
-                  else if constexpr (MASK == MASK_HALF)
-                    mv = (float)reinterpret_cast<const T*>(mrow)[kk] * kLog2e;
-                  else mv = reinterpret_cast<const float*>(mrow)[kk] * kLog2e;
+                  else if constexpr (MASK == MASK_HALF) mv = (float)reinterpret_cast<const T*>(mrow)[kk];
+                  else mv = reinterpret_cast<const float*>(mrow)[kk];
                 }
                 mval[kb][q4][e] = mv;
               }
             }
           }
       }
-
-      // S^T = K Q^T: two 32-key blocks, NS steps of 16 head-dim elements each.
-      f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 kop = lds_read16(Kt + koff[s & 3] + (s >> 2) * 128 + kb * 32 * KCH * 16);
-          sacc[kb] = Mfma16<T>::run(kop, qf[s], sacc[kb]);
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          bool ok = key < it.Lk;
+          if (CAUSAL) ok = ok && key <= qrow + it.shift;
+          float v = sc[kb][r];
+          if constexpr (MASK == MASK_BOOL) v += mval[kb][r >> 2][r & 3];
+          else if constexpr (MASK != MASK_NONE) v += mval[kb][r >> 2][r & 3] * a.inv_scale;
+          sc[kb][r] = ok ? v : -INFINITY;
         }
+    };
 
-      // Online softmax. Element r of block kb is key k0 + 32kb + 8(r/4) + 4hf + r%4.
-      float mt = -INFINITY;
-      if (!need_mask) {
+    // ---- pipeline pieces -------------------------------------------------------------------
+    // S^T = K Q^T for one tile, operand reads one step ahead (prologue only).
+    auto s_tile = [&](const WF_LDS char* Kt, f32x16* sc) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-        mt *= c;
-      } else {
+        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+      u32x4 k0f = kfrag(Kt, 0, 0), k1f = kfrag(Kt, 0, 1);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-            bool ok = key < it.Lk;
-            if (CAUSAL) ok = ok && key <= qrow + it.shift;
-            float t = sacc[kb][r] * c;
-            if constexpr (MASK != MASK_NONE) t += mval[kb][r >> 2][r & 3];
-            t = ok ? t : -INFINITY;
-            sacc[kb][r] = t;
-            mt = fmaxf(mt, t);
-          }
+      for (int s = 0; s < NS; ++s) {
+        u32x4 n0 = k0f, n1 = k1f;
+        if (s + 1 < NS) { n0 = kfrag(Kt, s + 1, 0); n1 = kfrag(Kt, s + 1, 1); }
+        sc[0] = Mfma16<T>::run(k0f, qf[s], sc[0]);
+        sc[1] = Mfma16<T>::run(k1f, qf[s], sc[1]);
+        k0f = n0; k1f = n1;
       }
-      mt = xhalf_max(mt);
+    };
+    // Tile max of the (masked, raw) scores in log2 units, reduced over both half-waves.
+    auto tile_max = [&](const f32x16* sc) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      return xhalf_max(mx) * c;
+    };
+    // Raise the reference max (rescaling O and l) only when a query's tile max passes it
+    // by more than 8, so p = exp2(t - m) stays <= 2^8.
+    auto rescale = [&](float mt) {
       if (wave_any(mt > m_run + 8.0f)) {
         const float m_new = fmaxf(m_run, mt);
         const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
@@ -291,64 +338,114 @@ struct AttnFwd {
           for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
         m_run = m_new;
       }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      float psum = 0.f;
-      if (!need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(sacc[kb][r], c, neg_m));
-            sacc[kb][r] = p;
-            psum += p;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(sacc[kb][r] + neg_m);
-            sacc[kb][r] = p;
-            psum += p;
-          }
-      }
-      l_run += psum;
-
-      // O^T += V^T P^T: 4 steps of 16 keys; step m uses elements 8(m%2).. of block m/2.
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = sacc[m >> 1][8 * (m & 1) + e];
-        const u32x4 pop = pack8<T>(pv);
-#pragma unroll
-        for (int n = 0; n < NDV; ++n) {
-          const WF_LDS char* base = Vt + voff[n & 1] + (n >> 1) * 128 + 16 * m * VCH * 16;
-          const u32x2 lo = lds_read_tr(base);
-          const u32x2 hi = lds_read_tr(base + 8 * VCH * 16);
-          const u32x4 vop = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[n] = Mfma16<T>::run(vop, pop, oacc[n]);
-        }
-      }
     };
 
-    // ---- key-tile loop: copy tile kt+1 while computing tile kt -------------------------
-    if (it.kt_lo < it.kt_hi) {
-      issue(it.kt_lo, sK0, sV0);
+    f32x16 sc[2], sn[2];  // scores of even / odd tiles (current and next alternate)
+    u32x4 pk[4];          // P^T operands of the current tile
+    float mt_cur = -INFINITY;
+
+    // Phase A: p = exp2(scale*log2e*s - m) for the current tile (packed to 16 bits as the
+    // P^T operand) while, if there is a next tile, its S^T MFMAs are issued in between.
+    auto phase_a = [&](const WF_LDS char* Kn, auto has_next_c, f32x16* cur, f32x16* nxt) {
+      constexpr bool has_next = decltype(has_next_c)::value;
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      float psum = 0.f;
+      if constexpr (has_next) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) nxt[kb][r] = 0.f;
+        u32x4 k0f = kfrag(Kn, 0, 0), k1f = kfrag(Kn, 0, 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          u32x4 n0 = k0f, n1 = k1f;
+          if (s + 1 < NS) { n0 = kfrag(Kn, s + 1, 0); n1 = kfrag(Kn, s + 1, 1); }
+          nxt[0] = Mfma16<T>::run(k0f, qf[s], nxt[0]);
+#pragma unroll
+          for (int e = s * 32 / NS; e < (s + 1) * 32 / NS; ++e) {
+            const float p = fast_exp2(fmaf(cur[e >> 4][e & 15], c, neg_m));
+            cur[e >> 4][e & 15] = p;
+            psum += p;
+          }
+          nxt[1] = Mfma16<T>::run(k1f, qf[s], nxt[1]);
+          k0f = n0; k1f = n1;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const float p = fast_exp2(fmaf(cur[e >> 4][e & 15], c, neg_m));
+          cur[e >> 4][e & 15] = p;
+          psum += p;
+        }
+      }
+      l_run += psum;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) pk[m] = pack8<T>(cur[m >> 1], 8 * (m & 1));
+    };
+
+    // Phase B: O^T += V^T P^T for the current tile while, if there is a next tile, its row
+    // max is folded in between the MFMAs.
+    auto phase_b = [&](const WF_LDS char* Vc, auto has_next_c, const f32x16* nxt) {
+      constexpr bool has_next = decltype(has_next_c)::value;
+      u32x4 vf[NDV];
+#pragma unroll
+      for (int n = 0; n < NDV; ++n) vf[n] = vfrag(Vc, 0, n);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        u32x4 vn[NDV];
+#pragma unroll
+        for (int n = 0; n < NDV; ++n) vn[n] = m + 1 < 4 ? vfrag(Vc, m + 1, n) : vf[n];
+#pragma unroll
+        for (int n = 0; n < NDV; ++n) oacc[n] = Mfma16<T>::run(vf[n], pk[m], oacc[n]);
+        if constexpr (has_next) {
+#pragma unroll
+          for (int e = 8 * m; e < 8 * m + 8; ++e) mx = fmaxf(mx, nxt[e >> 4][e & 15]);
+        }
+#pragma unroll
+        for (int n = 0; n < NDV; ++n) vf[n] = vn[n];
+      }
+      if constexpr (has_next) mt_cur = xhalf_max(mx) * c;
+    };
+
+    // ---- key-tile loop -----------------------------------------------------------------------
+    // Tile u (counted from kt_lo) has K in buffer u%2 and V in buffer u%2. Iteration u reads
+    // K_{u+1} (S^T of the next tile) and V_u, and copies K_{u+2} and V_{u+1} meanwhile.
+    const int n_tiles = it.kt_hi - it.kt_lo;
+    const int n_live = kt_live - it.kt_lo;
+    if (n_tiles > 0) {
+      issue_k(it.kt_lo, sK0);
+      issue_v(it.kt_lo, sV0);
+      if (n_tiles > 1) issue_k(it.kt_lo + 1, sK1);
       wait_vmem();
       __syncthreads();
-      int kt = it.kt_lo;
-      for (;;) {
-        if (kt + 1 < it.kt_hi) issue(kt + 1, sK1, sV1);
-        compute(kt, sK0, sV0);
+      if (n_live > 0) {
+        s_tile(sK0, sc);
+        if (need_mask(it.kt_lo)) apply_mask(it.kt_lo, sc);
+        mt_cur = tile_max(sc);
+      }
+      __syncthreads();  // K_0's buffer is refilled by the first iteration
+      auto iter = [&](int u, const WF_LDS char* Kn, WF_LDS char* Kfill, const WF_LDS char* Vc,
+                      WF_LDS char* Vfill, f32x16* cur, f32x16* nxt) {
+        if (u + 2 < n_tiles) issue_k(it.kt_lo + u + 2, Kfill);
+        if (u + 1 < n_tiles) issue_v(it.kt_lo + u + 1, Vfill);
+        if (u < n_live) {
+          // The next tile's S^T and row max are always computed: on this wave's last live
+          // tile they read a stale K buffer and the result is never used. This keeps both
+          // phases branch-free for the scheduler.
+          rescale(mt_cur);
+          phase_a(Kn, std::true_type(), cur, nxt);
+          if (u + 1 < n_live && need_mask(it.kt_lo + u + 1)) apply_mask(it.kt_lo + u + 1, nxt);
+          phase_b(Vc, std::true_type(), nxt);
+        }
         wait_vmem();
         __syncthreads();
-        if (++kt >= it.kt_hi) break;
-        if (kt + 1 < it.kt_hi) issue(kt + 1, sK0, sV0);
-        compute(kt, sK1, sV1);
-        wait_vmem();
-        __syncthreads();
-        if (++kt >= it.kt_hi) break;
+      };
+      for (int u = 0;;) {
+        iter(u, sK1, sK0, sV0, sV1, sc, sn);  // even tiles: scores in sc, next in sn
+        if (++u >= n_tiles) break;
+        iter(u, sK0, sK1, sV1, sV0, sn, sc);  // odd tiles: roles swapped
+        if (++u >= n_tiles) break;
       }
     }
 
@@ -390,21 +487,25 @@ struct AttnFwd {
 };
 
 // Work-group -> work-item decoding for the dense and split grids.
-// Dense: longest-first for causal (query tile rank major), and when B*Hkv is a multiple of
-// 8 the groups sharing one KV head are kept on one XCD (work groups are dealt to the 8 XCDs
-// round-robin by block index), so their K/V tiles are served from that XCD's L2.
+// Dense: longest-first for causal, and when B*Hkv is a multiple of 8 all work groups of one
+// KV group run on one XCD (work groups are dealt to the 8 XCDs round-robin by block index),
+// so their K/V tiles are served from that XCD's L2.
 template <class K, bool CAUSAL>
 __device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int split) {
   const int GH = a.G / K::kHPW;  // head groups per KV head
   const int nbg = a.B * a.Hkv;
   int hsub, bg, t_rank;
   if ((nbg & 7) == 0) {
+    // XCD x owns KV groups x, x+8, ...; it finishes one group (all its query tiles and
+    // head groups, longest first) before the next, so one group's K/V (Lk*d*4 bytes)
+    // is the L2 working set.
     const int x = bid & 7;
-    int s = bid >> 3;
-    hsub = s % GH; s /= GH;
-    const int nbgx = nbg >> 3;
-    bg = (s % nbgx) * 8 + x;
-    t_rank = s / nbgx;
+    const int s = bid >> 3;
+    const int per_group = a.n_qtiles * GH;
+    bg = (s / per_group) * 8 + x;
+    const int rem = s % per_group;
+    t_rank = rem / GH;
+    hsub = rem % GH;
   } else {
     hsub = bid % GH;
     const int s = bid / GH;
@@ -435,7 +536,8 @@ __device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int s
 }
 
 template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdArgs a) {
   typedef AttnFwd<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE> K;
   __shared__ __attribute__((aligned(1024))) char sK0[K::KBYTES];
   __shared__ __attribute__((aligned(1024))) char sK1[K::KBYTES];

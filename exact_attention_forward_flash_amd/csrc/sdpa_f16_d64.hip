@@ -7,6 +7,8 @@ static const AttnEntry kTable[] = {
     E(8, 1, MASK_NONE, false), E(8, 2, MASK_NONE, false), E(8, 4, MASK_NONE, false),
     E(8, 1, MASK_NONE, true),  E(8, 2, MASK_NONE, true),  E(8, 4, MASK_NONE, true),
     E(8, 1, MASK_BOOL, false), E(8, 1, MASK_HALF, false), E(8, 1, MASK_F32, false),
+    E(4, 1, MASK_NONE, false), E(4, 2, MASK_NONE, false), E(4, 4, MASK_NONE, false),
+    E(4, 1, MASK_NONE, true),  E(4, 2, MASK_NONE, true),  E(4, 4, MASK_NONE, true),
 };
 #undef E
 const AttnEntry* attn_table_sdpa_f16_d64(int* n) {

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -184,6 +185,7 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   a.causal_shift = 0;
   a.mask_vec = mask_vec ? 1 : 0;
   a.scale_log2 = scale * wf::kLog2e;
+  a.inv_scale = 1.0f / scale;
   const int dt = kernel_dtype(q->dtype);
   if (dt == wf::DT_F32) {
     const wf::F32Entry* e = find_f32(Dqk, Dv, mask_kind, causal);
@@ -195,7 +197,10 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   }
   int hpw = 1;
   if (mask_kind == wf::MASK_NONE) hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const wf::AttnEntry* e = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, mask_kind, causal, wf::MODE_DENSE);
+  int nw = 8;
+  if (const char* t = getenv("WF_TUNE_NW")) nw = atoi(t) == 4 && mask_kind == wf::MASK_NONE ? 4 : 8;
+  if (const char* t = getenv("WF_TUNE_HPW")) { int h = atoi(t); if (h >= 1 && h <= hpw && G % h == 0) hpw = h; }
+  const wf::AttnEntry* e = find_attn(dt, Dqk, Dqk, Dv, nw, hpw, mask_kind, causal, wf::MODE_DENSE);
   if (!e) return fail(WF_ERR_UNSUPPORTED, "no 16-bit kernel for Dqk=%d Dv=%d", Dqk, Dv);
   a.n_qtiles = (Lq + e->bmp - 1) / e->bmp;
   const int64_t blocks = (int64_t)a.n_qtiles * B * Hkv * (G / hpw);
@@ -402,6 +407,7 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
   a.o_sm = out.stride[0]; a.o_sh = out.stride[1];
   a.B = batch; a.Hq = head_num; a.Hkv = kv_head_num; a.G = head_num / kv_head_num;
   a.scale_log2 = sc * wf::kLog2e;
+  a.inv_scale = 1.0f / sc;
   a.cu_q = (const int*)((char*)workspace + wf::VarlenWs::cu_q_off());
   a.cu_k = (const int*)((char*)workspace + wf::VarlenWs::cu_k_off(batch));
   a.items = (const int2*)((char*)workspace + wf::VarlenWs::items_off(batch));
@@ -577,6 +583,7 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   a.Lk = (int)n_vis;
   a.n_qtiles = n_qt;
   a.scale_log2 = sc * wf::kLog2e;
+  a.inv_scale = 1.0f / sc;
   a.tiles_per_split = tps;
   const int64_t rows = B * Hq * Lq;
   a.part_o = (float*)workspace;

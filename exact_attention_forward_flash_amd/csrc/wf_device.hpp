@@ -47,11 +47,11 @@ template <> struct Mfma16<_Float16> {
 
 // Round 8 fp32 values to the 16-bit type (nearest even) and pack them as an MFMA operand.
 template <typename T>
-__device__ __forceinline__ u32x4 pack8(const float* p) {
+__device__ __forceinline__ u32x4 pack8(const f32x16& p, int off) {
   typedef typename Mfma16<T>::v8 v8;
   v8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (T)p[e];
+  for (int e = 0; e < 8; ++e) r[e] = (T)p[off + e];
   return __builtin_bit_cast(u32x4, r);
 }
 
