@@ -57,8 +57,8 @@ def measured_traffic():
 
 
 def cpu_baseline():
-    """The fp64 oracle on a bounded sample: batch 0, query heads 0-7 (KV heads 0-1), all 4096
-    rows, causal. Throughput in the metric's unit over the sample's algorithmic flops."""
+    """The fp64 oracle on a bounded sample: batches 0-2 (96 query heads, 24 KV heads), all
+    4096 rows, causal. Throughput in the metric's unit over the sample's algorithmic flops."""
     import numpy as np
     import oracle
     from synth import causal_gqa_prefill
@@ -68,17 +68,46 @@ def cpu_baseline():
     except Exception:
         cores = os.cpu_count()
     w = causal_gqa_prefill()
-    heads = 8
-    q = w["q"][0:1, 0:heads]
-    k = w["k"][0:1, 0:heads // 4]
-    v = w["v"][0:1, 0:heads // 4]
+    nb = 3
+    q, k, v = w["q"][:nb], w["k"][:nb], w["v"][:nb]
     t0 = time.perf_counter()
     oracle.sdpa(q, k, v, is_causal=True, scale=np.float32(w["scale"]))
     dt = time.perf_counter() - t0
-    fl = flops_per_step(1, heads, CFG["L"], CFG["D"], True)
+    fl = flops_per_step(nb, CFG["Hq"], CFG["L"], CFG["D"], True)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"batch 0, query heads 0-{heads - 1} (kv heads 0-{heads // 4 - 1}), "
-                      f"all {CFG['L']} rows, causal, fp64 numpy; {dt:.1f} s"}
+            "sample": f"batches 0-{nb - 1} of the workload ({nb * CFG['Hq']} query heads), all "
+                      f"{CFG['L']} rows, causal, fp64 numpy oracle; {dt:.1f} s wall"}
+
+
+def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Turns rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs (KiB per dispatch) of the
+    attention kernel and of the plain 256 MiB copy (--copy-calibration) into HBM bytes per
+    launch: each counter is scaled by (copy bytes) / (what it reads for the copy)."""
+    import csv
+
+    def per_dispatch(path, name_part):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if name_part in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no {name_part} dispatch in {path}")
+        vals.sort()
+        return vals[len(vals) // 2] * 1024.0  # median, bytes
+
+    copy_bytes = 256 << 20
+    f_scale = copy_bytes / per_dispatch(copy_fetch_csv, "copyBuffer")
+    w_scale = copy_bytes / per_dispatch(copy_write_csv, "copyBuffer")
+    rd = per_dispatch(fetch_csv, "attn_fwd_kernel") * f_scale
+    wr = per_dispatch(write_csv, "attn_fwd_kernel") * w_scale
+    B, Hq, Hkv, L, D = (CFG[x] for x in ("B", "Hq", "Hkv", "L", "D"))
+    algo_rd = 2 * (B * Hq * L * D + 2 * B * Hkv * L * D)
+    algo_wr = 2 * B * Hq * L * D
+    rec = {"kernel_source_hash": kernel_source_hash(), "hbm_bytes_per_launch": int(rd + wr),
+           "read_bytes": int(rd), "write_bytes": int(wr),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "algorithmic_read_bytes": algo_rd, "algorithmic_write_bytes": algo_wr}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def main():
@@ -87,10 +116,16 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
+                    help="FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter CSVs "
+                         "from rocprofv3 --pmc: record HBM bytes per launch and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 3 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the attention path here has no multi-GPU mode "
               "(run with --gpus 1)", file=sys.stderr)

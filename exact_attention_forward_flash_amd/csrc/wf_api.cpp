@@ -10,7 +10,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/wf.h"
+#include "wf.h"
 #include "wf_internal.hpp"
 
 namespace {
