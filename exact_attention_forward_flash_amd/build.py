@@ -33,9 +33,18 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
+# 64-query-wave kernels: MFMAs the compiler generates keep VGPR accumulators (their O^T
+# accumulators are placed in AGPRs explicitly).
+W64_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+
+
+def flags_for(src):
+    return FLAGS + (W64_FLAGS if src.endswith("_w64.hip") else [])
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *flags_for(src), "-c", src, "-o", obj]
     t0 = time.time()
     p = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

@@ -62,6 +62,21 @@ struct WorkItem {
   int64_t qtok0, ktok0;
 };
 
+// LDS swizzles (chunk position = chunk ^ swizzle(row)) for tiles of CH 16-byte chunks per
+// row. They keep the MFMA operand reads conflict-free whether the LDS serves 128 or 256
+// bytes per clock:
+//  K (16-byte reads, lane -> row): any 8 and any 16 consecutive rows get distinct banks.
+//  V (8-byte transpose reads over 4 consecutive rows x 2 or 4 chunks): the 4 rows of a
+//    16-lane group and of a 32-lane group land on distinct banks.
+template <int CH>
+__device__ __forceinline__ int lds_kswz(int row) {
+  return CH == 16 ? (row & 15) : ((row ^ ((row >> 3) & 3)) & 7);  // period 32 in row
+}
+template <int CH>
+__device__ __forceinline__ int lds_vswz(int row) {
+  return CH == 16 ? (((row & 1) * 6) ^ ((row & 2) * 5)) : 2 * (row & 3);
+}
+
 template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
 struct AttnFwd {
   static constexpr int BN = 64;
@@ -83,17 +98,8 @@ struct AttnFwd {
   static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile copies split evenly");
   static_assert(KCH % 8 == 0 && VCH % 8 == 0 && DQK1 % 16 == 0 && DV % 32 == 0, "tile shape");
 
-  // LDS swizzles (chunk position = chunk ^ swizzle(row)). They keep the MFMA operand reads
-  // conflict-free whether the LDS serves 128 or 256 bytes per clock:
-  //  K (16-byte reads, lane -> row): any 8 and any 16 consecutive rows get distinct banks.
-  //  V (8-byte transpose reads over 4 consecutive rows x 2 or 4 chunks): the 4 rows of a
-  //    16-lane group and of a 32-lane group land on distinct banks.
-  static __device__ __forceinline__ int kswz(int row) {
-    return KCH == 16 ? (row & 15) : ((row ^ ((row >> 3) & 3)) & 7);  // period 32 in row
-  }
-  static __device__ __forceinline__ int vswz(int row) {
-    return VCH == 16 ? (((row & 1) * 6) ^ ((row & 2) * 5)) : 2 * (row & 3);
-  }
+  static __device__ __forceinline__ int kswz(int row) { return lds_kswz<KCH>(row); }
+  static __device__ __forceinline__ int vswz(int row) { return lds_vswz<VCH>(row); }
 
   // Number of key tiles a work group covering positions [pos0, pos0 + BMP) must visit.
   static __device__ __forceinline__ int tile_end(int pos0, int Lk, int shift) {
@@ -535,21 +541,14 @@ __device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int s
   return it;
 }
 
-template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_kernel(FwdArgs a) {
-  typedef AttnFwd<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE> K;
-  __shared__ __attribute__((aligned(1024))) char sK0[K::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[K::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[K::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[K::VBYTES];
-  WF_LDS char* k0 = (WF_LDS char*)sK0;
-  WF_LDS char* k1 = (WF_LDS char*)sK1;
-  WF_LDS char* v0 = (WF_LDS char*)sV0;
-  WF_LDS char* v1 = (WF_LDS char*)sV1;
+// Work distribution shared by the kernel shapes: a persistent loop over the device-built
+// schedule (varlen), or one work item per work group (dense, split). run_item(it) runs one
+// work item with the kernel's LDS buffers.
+template <class K, int MODE, bool CAUSAL, class RunItem>
+__device__ __forceinline__ void attn_dispatch(const FwdArgs& a, const RunItem& run_item) {
   if constexpr (MODE == MODE_VARLEN) {
     __shared__ int s_item;
-    const int NHG = a.Hq / HPW;            // head groups per (sequence, query tile) item
+    const int NHG = a.Hq / K::kHPW;        // head groups per (sequence, query tile) item
     const int n_work = *a.n_items * NHG;
     for (;;) {
       if (threadIdx.x == 0) s_item = atomicAdd(a.counter, 1);
@@ -559,7 +558,7 @@ void attn_fwd_kernel(FwdArgs a) {
       const int2 pr = a.items[idx / NHG];
       WorkItem it;
       it.b = pr.x;
-      it.hq0 = (idx % NHG) * HPW;
+      it.hq0 = (idx % NHG) * K::kHPW;
       it.pos0 = pr.y * K::BMP;
       const int cq0 = a.cu_q[it.b], ck0 = a.cu_k[it.b];
       it.Lq = a.cu_q[it.b + 1] - cq0;
@@ -570,16 +569,29 @@ void attn_fwd_kernel(FwdArgs a) {
       it.split = -1;
       it.kt_lo = 0;
       it.kt_hi = K::tile_end(it.pos0, it.Lk, it.shift);
-      K::run(a, it, k0, k1, v0, v1);
+      run_item(it);
       __syncthreads();
     }
   } else if constexpr (MODE == MODE_SPLIT) {
     const WorkItem it = decode_grid<K, CAUSAL>(a, blockIdx.x, blockIdx.y);
-    K::run(a, it, k0, k1, v0, v1);
+    run_item(it);
   } else {
     const WorkItem it = decode_grid<K, CAUSAL>(a, blockIdx.x, -1);
-    K::run(a, it, k0, k1, v0, v1);
+    run_item(it);
   }
+}
+
+template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdArgs a) {
+  typedef AttnFwd<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE> K;
+  __shared__ __attribute__((aligned(1024))) char sK0[K::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[K::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[K::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[K::VBYTES];
+  attn_dispatch<K, MODE, CAUSAL>(a, [&](const WorkItem& it) {
+    K::run(a, it, (WF_LDS char*)sK0, (WF_LDS char*)sK1, (WF_LDS char*)sV0, (WF_LDS char*)sV1);
+  });
 }
 
 }  // namespace wf

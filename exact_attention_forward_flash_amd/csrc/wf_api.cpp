@@ -104,12 +104,15 @@ int check_cache_data(const wf_tensor* t, const char* name, bool* unit16) {
   return WF_OK;
 }
 
+// qpw: queries per wave (32 or 64), 0 = any. nw, hpw: 0 = any.
 const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int hpw, int mask,
-                               int causal, int mode) {
+                               int causal, int mode, int qpw = 32) {
   typedef const wf::AttnEntry* (*TableFn)(int*);
   static const TableFn tables[] = {wf::attn_table_sdpa_bf16_d64, wf::attn_table_sdpa_bf16_d128,
                                    wf::attn_table_sdpa_f16_d64,  wf::attn_table_sdpa_f16_d128,
-                                   wf::attn_table_mla,           wf::attn_table_split};
+                                   wf::attn_table_mla,           wf::attn_table_split,
+                                   wf::attn_table_w_bf16_d64,    wf::attn_table_w_bf16_d128,
+                                   wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128};
   for (TableFn f : tables) {
     int n = 0;
     const wf::AttnEntry* t = f(&n);
@@ -117,7 +120,7 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
       const wf::AttnEntry& e = t[i];
       if (e.dtype == dtype && e.dqk == dqk && e.dqk1 == dqk1 && e.dv == dv &&
           (nw == 0 || e.nw == nw) && (hpw == 0 || e.hpw == hpw) && e.mask == mask &&
-          e.causal == causal && e.mode == mode)
+          e.causal == causal && e.mode == mode && (qpw == 0 || e.qpw == qpw))
         return &e;
     }
   }
@@ -197,10 +200,20 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   }
   int hpw = 1;
   if (mask_kind == wf::MASK_NONE) hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  int nw = 8;
-  if (const char* t = getenv("WF_TUNE_NW")) nw = atoi(t) == 4 && mask_kind == wf::MASK_NONE ? 4 : 8;
   if (const char* t = getenv("WF_TUNE_HPW")) { int h = atoi(t); if (h >= 1 && h <= hpw && G % h == 0) hpw = h; }
-  const wf::AttnEntry* e = find_attn(dt, Dqk, Dqk, Dv, nw, hpw, mask_kind, causal, wf::MODE_DENSE);
+  // Kernel shape: 64-query waves (one per SIMD) for non-causal calls without the log-sum-exp
+  // (their row sums are taken over the 16-bit weights: exact for the normalised output, but
+  // the sum, and so the lse, keeps the 16-bit rounding; the 32-query kernel sums in fp32);
+  // 32-query waves otherwise. WF_TUNE_QPW=32|64 overrides.
+  int qpw = (lse == nullptr && !causal) ? 64 : 32;
+  if (const char* t = getenv("WF_TUNE_QPW")) qpw = atoi(t) == 32 ? 32 : atoi(t) == 64 ? 64 : qpw;
+  const wf::AttnEntry* e = nullptr;
+  if (qpw == 64) e = find_attn(dt, Dqk, Dqk, Dv, 4, hpw, mask_kind, causal, wf::MODE_DENSE, 64);
+  if (!e) {
+    int nw = 8;
+    if (const char* t = getenv("WF_TUNE_NW")) nw = atoi(t) == 4 && mask_kind == wf::MASK_NONE ? 4 : 8;
+    e = find_attn(dt, Dqk, Dqk, Dv, nw, hpw, mask_kind, causal, wf::MODE_DENSE, 32);
+  }
   if (!e) return fail(WF_ERR_UNSUPPORTED, "no 16-bit kernel for Dqk=%d Dv=%d", Dqk, Dv);
   a.n_qtiles = (Lq + e->bmp - 1) / e->bmp;
   const int64_t blocks = (int64_t)a.n_qtiles * B * Hkv * (G / hpw);

@@ -77,6 +77,10 @@ __device__ __forceinline__ void dma16(const void* g, WF_LDS char* lds_wave_base)
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory loads of this wave are outstanding (they complete in
+// issue order): everything but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 __device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
 

@@ -4,14 +4,16 @@
 #include <stdint.h>
 
 #include "attn_fwd.hpp"
+#include "attn_fwd_w.hpp"
 
 namespace wf {
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
-// One compiled instantiation of attn_fwd_kernel.
+// One compiled instantiation of attn_fwd_kernel (32 queries per wave) or attn_fwd_w_kernel
+// (64 queries per wave).
 struct AttnEntry {
-  int dtype, dqk, dqk1, dv, nw, hpw, mask, causal, mode;
+  int dtype, dqk, dqk1, dv, nw, qpw, hpw, mask, causal, mode;
   const void* fn;   // __global__ void(FwdArgs)
   int bmp;          // query positions per work group
   int bn;           // keys per tile
@@ -24,11 +26,22 @@ const AttnEntry* attn_table_sdpa_f16_d64(int* n);
 const AttnEntry* attn_table_sdpa_f16_d128(int* n);
 const AttnEntry* attn_table_mla(int* n);
 const AttnEntry* attn_table_split(int* n);
+const AttnEntry* attn_table_w_bf16_d128(int* n);
+const AttnEntry* attn_table_w_bf16_d64(int* n);
+const AttnEntry* attn_table_w_f16_d128(int* n);
+const AttnEntry* attn_table_w_f16_d64(int* n);
 
 #define WF_ATTN_ENTRY(T, DT, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE)                     \
-  {DT, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE,                                          \
+  {DT, DQK, DQK1, DV, NW, 32, HPW, MASK, CAUSAL, MODE,                                      \
    (const void*)&attn_fwd_kernel<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE>,             \
    AttnFwd<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE>::BMP, 64}
+
+// Translation units holding 64-query-wave instantiations are compiled with the MFMA VGPR
+// form forced for compiler-generated MFMAs (the S^T products), see attn_fwd_w.hpp.
+#define WF_ATTN_W_ENTRY(T, DT, DQK, DQK1, DV, HPW, MASK, CAUSAL, MODE)                       \
+  {DT, DQK, DQK1, DV, 4, 64, HPW, MASK, CAUSAL, MODE,                                       \
+   (const void*)&attn_fwd_w_kernel<T, DQK, DQK1, DV, HPW, MASK, CAUSAL, MODE>,               \
+   AttnFwdW<T, DQK, DQK1, DV, HPW, MASK, CAUSAL, MODE>::BMP, 64}
 
 // fp32 path (MFMA 32x32x2 f32).
 struct F32Entry {

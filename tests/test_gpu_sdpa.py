@@ -47,8 +47,10 @@ CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, causal
 def test_random_shapes(case):
     dt, B, Hq, Hkv, Lq, Lk, D, causal = case
     w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 1000)
-    out, lse = run(w, is_causal=causal, return_lse=True)
     ref, ref_lse = oracle.sdpa(w["q"], w["k"], w["v"], is_causal=causal, scale=np.float32(w["scale"]))
+    out = run(w, is_causal=causal)
+    assert_close(out, ref, w["q"].dtype, str(case) + " (no lse)")
+    out, lse = run(w, is_causal=causal, return_lse=True)
     assert_close(out, ref, w["q"].dtype, str(case))
     live = np.isfinite(ref_lse)
     assert np.array_equal(np.isfinite(to64(lse)), live)
@@ -114,9 +116,38 @@ def test_fully_masked_rows_and_empty_keys():
     assert np.all(np.isneginf(to64(lse)[:, :, [7, 33]]))
     ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=m, scale=np.float32(w["scale"]))
     assert_close(out, ref, torch.bfloat16, "fully masked rows")
+    out = run(w)  # without lse
+    o = to64(out)
+    assert np.all(o[:, :, 7] == 0) and np.all(o[:, :, 33] == 0)
+    assert_close(out, ref, torch.bfloat16, "fully masked rows (no lse)")
     w0 = random_sdpa_inputs(1, 2, 2, 40, 0, 64, 64, "bf16", seed=6)
     out0 = run(w0)
     assert out0.shape == (1, 2, 40, 64) and torch.all(out0 == 0)
+
+
+# Both kernel shapes on every case, whatever the default choice for it: 64-query waves (one
+# per SIMD, row sums over the 16-bit weights) and 32-query waves (two per SIMD). The shape
+# is picked per call from WF_TUNE_QPW.
+SHAPE_CASES = [c + (m,) for c in CASES for m in (None,)] + [
+    ("bf16", 2, 4, 4, 130, 301, 128, False, "bool"),
+    ("fp16", 2, 4, 4, 97, 200, 64, False, "half"),
+    ("bf16", 1, 4, 4, 64, 128, 128, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("qpw", [64, 32])
+@pytest.mark.parametrize("case", SHAPE_CASES, ids=[str(c) for c in SHAPE_CASES])
+def test_kernel_shapes(case, qpw, monkeypatch):
+    dt, B, Hq, Hkv, Lq, Lk, D, causal, mkind = case
+    w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 997)
+    if mkind is not None:
+        g = torch.Generator().manual_seed(21)
+        w["mask"] = _mask(mkind, "b1", B, Hq, Lq, Lk, w["q"].dtype, g)
+    ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w.get("mask"), is_causal=causal,
+                         scale=np.float32(w["scale"]))
+    monkeypatch.setenv("WF_TUNE_QPW", str(qpw))
+    out = run(w, is_causal=causal)
+    assert_close(out, ref, w["q"].dtype, f"{case} qpw={qpw}")
 
 
 def test_deterministic():
@@ -144,9 +175,13 @@ def _sampled_rows_causal(w, out, picks, rows):
             assert_close(out[b:b + 1, h:h + 1, i0:i1], ref, q.dtype, f"b{b} h{h} rows {i0}:{i1}")
 
 
-def test_causal_gqa_prefill_full_size_sampled():
-    """B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal, in the benchmark's launch configuration;
-    sampled rows across the sequence checked against the oracle."""
+@pytest.mark.parametrize("qpw", [None, 64])
+def test_causal_gqa_prefill_full_size_sampled(qpw, monkeypatch):
+    """B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal, in the benchmark's launch configuration
+    (qpw None) and with 64-query waves; sampled rows across the sequence checked against the
+    oracle."""
+    if qpw is not None:
+        monkeypatch.setenv("WF_TUNE_QPW", str(qpw))
     w = causal_gqa_prefill()
     out = run(w, is_causal=True)
     assert tuple(out.shape) == (4, 32, 4096, 128)
