@@ -3,6 +3,7 @@
 // Validation completes before anything is enqueued; a failing call changes nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -204,9 +205,12 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   // Kernel shape: 64-query waves (one per SIMD) for non-causal calls without the log-sum-exp
   // (their row sums are taken over the 16-bit weights: exact for the normalised output, but
   // the sum, and so the lse, keeps the 16-bit rounding; the 32-query kernel sums in fp32);
-  // 32-query waves otherwise. WF_TUNE_QPW=32|64 overrides.
-  int qpw = (lse == nullptr && !causal) ? 64 : 32;
-  if (const char* t = getenv("WF_TUNE_QPW")) qpw = atoi(t) == 32 ? 32 : atoi(t) == 64 ? 64 : qpw;
+  // 32-query waves otherwise. The 64-query kernel keeps its K/V copy offsets in 32 bits, so
+  // 64 rows of K and of V must span less than 2 GiB. WF_TUNE_QPW=32|64 overrides.
+  const int64_t max_sm = std::max(k->stride[2], v->stride[2]);
+  const bool w64_ok = max_sm >= 0 && max_sm * 2 * 64 < ((int64_t)1 << 31);
+  int qpw = (lse == nullptr && !causal && w64_ok) ? 64 : 32;
+  if (const char* t = getenv("WF_TUNE_QPW")) qpw = atoi(t) == 32 ? 32 : (atoi(t) == 64 && w64_ok) ? 64 : qpw;
   const wf::AttnEntry* e = nullptr;
   if (qpw == 64) e = find_attn(dt, Dqk, Dqk, Dv, 4, hpw, mask_kind, causal, wf::MODE_DENSE, 64);
   if (!e) {

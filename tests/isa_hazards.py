@@ -1,0 +1,100 @@
+"""Wait-state checks on generated gfx950 code for the instructions the 64-query-wave kernel
+writes as inline asm (the compiler's hazard recognizer does not look inside inline asm):
+
+  * an MFMA with an AGPR accumulator must be >= 2 wait states after a VALU write of any of
+    its sources;
+  * no non-MFMA instruction may touch such an MFMA's accumulator within 12 wait states after
+    it (16 are issued);
+  * an ordinary VALU read of a v_dot2c result must be >= 3 wait states after it (a following
+    v_dot2c accumulating into it is fine).
+
+Each instruction counts one wait state, s_nop N counts N + 1. Linear scan per kernel
+(labels are fall-through)."""
+import re
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def _parse(line):
+    t = line.strip()
+    if not t or t.startswith((";", ".")) or t.endswith(":"):
+        return None
+    t = t.split(";")[0].strip()
+    parts = t.split(None, 1)
+    ops = [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
+    return parts[0], ops
+
+
+def check_kernel(lines):
+    """Returns a list of hazard descriptions for one kernel's instruction lines."""
+    insts = [p for p in (_parse(l) for l in lines) if p]
+    bad = []
+    for i, (op, ops) in enumerate(insts):
+        if op.startswith("v_mfma") and ops and ops[0].startswith("a["):
+            srcs = set().union(*(_regs(o) for o in ops[1:]))
+            ws = 0
+            for j in range(i - 1, max(-1, i - 8), -1):
+                pop, pops = insts[j]
+                if pop == "s_nop":
+                    ws += int(pops[0]) + 1
+                    continue
+                if ws >= 2:
+                    break
+                if pop.startswith("v_") and not pop.startswith("v_mfma") and pops and _regs(pops[0]) & srcs:
+                    bad.append(f"VALU write {pop} {pops[0]} then {op} {','.join(ops)}")
+                ws += 1
+            dst = _regs(ops[0])
+            ws = 0
+            for j in range(i + 1, min(len(insts), i + 40)):
+                pop, pops = insts[j]
+                if pop == "s_nop":
+                    ws += int(pops[0]) + 1
+                    continue
+                if ws >= 12:
+                    break
+                if not pop.startswith("v_mfma") and pops and set().union(*(_regs(o) for o in pops)) & dst:
+                    bad.append(f"{op} {ops[0]} then {pop} {','.join(pops)}")
+                ws += 1
+        if op.startswith("v_dot2c") and ops:
+            dst = _regs(ops[0])
+            ws = 0
+            for j in range(i + 1, min(len(insts), i + 10)):
+                pop, pops = insts[j]
+                if pop == "s_nop":
+                    ws += int(pops[0]) + 1
+                    continue
+                if ws >= 3:
+                    break
+                if pop.startswith("v_") and not pop.startswith("v_dot2c") and len(pops) > 1 and \
+                        set().union(*(_regs(o) for o in pops[1:])) & dst:
+                    bad.append(f"{op} {ops[0]} then {pop} {','.join(pops)}")
+                ws += 1
+    return bad
+
+
+def check_asm(text):
+    """{kernel name: [hazards]} for every kernel symbol in an assembly listing."""
+    out, name, cur = {}, None, []
+    for l in text.splitlines():
+        m = re.match(r"^(_Z\w+):", l)
+        if m:
+            if name:
+                out[name] = check_kernel(cur)
+            name, cur = m.group(1), []
+        elif name:
+            if l.startswith(".Lfunc_end"):
+                out[name] = check_kernel(cur)
+                name, cur = None, []
+            else:
+                cur.append(l)
+    if name:
+        out[name] = check_kernel(cur)
+    return out
