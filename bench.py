@@ -25,9 +25,12 @@ METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak (causal GQA prefill, 4k)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 CFG = dict(B=4, Hq=32, Hkv=8, L=4096, D=128)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_causal_gqa_4k_traffic.json")
+# Sources of the kernel the benchmark launches (the persistent 32-query kernel).
 KERNEL_SOURCES = ["exact_attention_forward_flash_amd/csrc/attn_fwd.hpp",
+                  "exact_attention_forward_flash_amd/csrc/attn_fwd_p.hpp",
                   "exact_attention_forward_flash_amd/csrc/wf_device.hpp",
-                  "exact_attention_forward_flash_amd/csrc/sdpa_bf16_d128.hip"]
+                  "exact_attention_forward_flash_amd/csrc/sdpa_bf16_d128_p.hip"]
+KERNEL_NAME = "attn_fwd_p_kernel"
 
 
 def flops_per_step(B, Hq, L, D, causal=True):
@@ -96,8 +99,8 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     copy_bytes = 256 << 20
     f_scale = copy_bytes / per_dispatch(copy_fetch_csv, "copyBuffer")
     w_scale = copy_bytes / per_dispatch(copy_write_csv, "copyBuffer")
-    rd = per_dispatch(fetch_csv, "attn_fwd_kernel") * f_scale
-    wr = per_dispatch(write_csv, "attn_fwd_kernel") * w_scale
+    rd = per_dispatch(fetch_csv, KERNEL_NAME) * f_scale
+    wr = per_dispatch(write_csv, KERNEL_NAME) * w_scale
     B, Hq, Hkv, L, D = (CFG[x] for x in ("B", "Hq", "Hkv", "L", "D"))
     algo_rd = 2 * (B * Hq * L * D + 2 * B * Hkv * L * D)
     algo_wr = 2 * B * Hq * L * D
@@ -113,8 +116,10 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU's clocks settle over the first few dozen launches (a launch takes ~0.6 ms):
+    # 100 untimed launches precede the 200 timed ones.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter CSVs "

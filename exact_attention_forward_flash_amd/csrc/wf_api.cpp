@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -113,7 +114,9 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
                                    wf::attn_table_sdpa_f16_d64,  wf::attn_table_sdpa_f16_d128,
                                    wf::attn_table_mla,           wf::attn_table_split,
                                    wf::attn_table_w_bf16_d64,    wf::attn_table_w_bf16_d128,
-                                   wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128};
+                                   wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128,
+                                   wf::attn_table_p_bf16_d64,    wf::attn_table_p_bf16_d128,
+                                   wf::attn_table_p_f16_d64,     wf::attn_table_p_f16_d128};
   for (TableFn f : tables) {
     int n = 0;
     const wf::AttnEntry* t = f(&n);
@@ -148,6 +151,21 @@ int device_cus() {
     cache[dev] = n;
   }
   return cache[dev];
+}
+
+// Compute units of the current device (0 if the query fails), cached per device.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 hipError_t launch(const void* fn, dim3 grid, dim3 block, wf::FwdArgs& a, hipStream_t s) {
@@ -209,6 +227,24 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   // 64 rows of K and of V must span less than 2 GiB. WF_TUNE_QPW=32|64 overrides.
   const int64_t max_sm = std::max(k->stride[2], v->stride[2]);
   const bool w64_ok = max_sm >= 0 && max_sm * 2 * 64 < ((int64_t)1 << 31);
+  // Persistent form of the 32-query kernel (one work group per CU walking a list of work
+  // items): calls without a mask whose Q/K/V copy offsets fit in 32 bits and, when causal,
+  // whose work groups cover one 64-key tile of query positions (HPW = 4). WF_TUNE_PERSIST=0
+  // turns it off.
+  const bool q_ok = q->stride[2] >= 0 && q->stride[2] * 2 * 32 < ((int64_t)1 << 31);
+  bool persist = mask_kind == wf::MASK_NONE && Lk > 0 && w64_ok && q_ok && (!causal || hpw == 4);
+  if (const char* t = getenv("WF_TUNE_PERSIST")) persist = persist && atoi(t) != 0;
+  if (persist) {
+    const wf::AttnEntry* pe = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, wf::MASK_NONE, causal, wf::MODE_DENSE_P);
+    const int ncu = cu_count();
+    if (pe != nullptr && ncu > 0) {
+      a.n_qtiles = (Lq + pe->bmp - 1) / pe->bmp;
+      const int64_t items = (int64_t)a.n_qtiles * B * Hkv * (G / hpw);
+      const int64_t P = std::min<int64_t>(ncu, items);
+      if (P > 0 && (items + P - 1) / P <= wf::kPersistMaxItems)
+        return hip_status(launch(pe->fn, dim3((unsigned)P), dim3(512), a, stream), "attention launch");
+    }
+  }
   int qpw = (lse == nullptr && !causal && w64_ok) ? 64 : 32;
   if (const char* t = getenv("WF_TUNE_QPW")) qpw = atoi(t) == 32 ? 32 : (atoi(t) == 64 && w64_ok) ? 64 : qpw;
   const wf::AttnEntry* e = nullptr;

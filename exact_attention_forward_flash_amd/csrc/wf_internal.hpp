@@ -5,6 +5,7 @@
 
 #include "attn_fwd.hpp"
 #include "attn_fwd_w.hpp"
+#include "attn_fwd_p.hpp"
 
 namespace wf {
 
@@ -30,6 +31,10 @@ const AttnEntry* attn_table_w_bf16_d128(int* n);
 const AttnEntry* attn_table_w_bf16_d64(int* n);
 const AttnEntry* attn_table_w_f16_d128(int* n);
 const AttnEntry* attn_table_w_f16_d64(int* n);
+const AttnEntry* attn_table_p_bf16_d128(int* n);
+const AttnEntry* attn_table_p_bf16_d64(int* n);
+const AttnEntry* attn_table_p_f16_d128(int* n);
+const AttnEntry* attn_table_p_f16_d64(int* n);
 
 #define WF_ATTN_ENTRY(T, DT, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE)                     \
   {DT, DQK, DQK1, DV, NW, 32, HPW, MASK, CAUSAL, MODE,                                      \
@@ -42,6 +47,13 @@ const AttnEntry* attn_table_w_f16_d64(int* n);
   {DT, DQK, DQK1, DV, 4, 64, HPW, MASK, CAUSAL, MODE,                                       \
    (const void*)&attn_fwd_w_kernel<T, DQK, DQK1, DV, HPW, MASK, CAUSAL, MODE>,               \
    AttnFwdW<T, DQK, DQK1, DV, HPW, MASK, CAUSAL, MODE>::BMP, 64}
+
+// Persistent dense kernel (32 queries per wave, 8 waves, no mask): one work group per CU
+// walks its list of at most AttnFwdP<...>::MAX_ITEMS work items.
+#define WF_ATTN_P_ENTRY(T, DT, D, HPW, CAUSAL)                                               \
+  {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL, MODE_DENSE_P,                                \
+   (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL>, AttnFwdP<T, D, D, HPW, CAUSAL>::BMP, 64}
+constexpr int kPersistMaxItems = AttnFwdP<__bf16, 128, 128, 4, false>::MAX_ITEMS;
 
 // fp32 path (MFMA 32x32x2 f32).
 struct F32Entry {

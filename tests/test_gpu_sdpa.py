@@ -125,9 +125,11 @@ def test_fully_masked_rows_and_empty_keys():
     assert out0.shape == (1, 2, 40, 64) and torch.all(out0 == 0)
 
 
-# Both kernel shapes on every case, whatever the default choice for it: 64-query waves (one
-# per SIMD, row sums over the 16-bit weights) and 32-query waves (two per SIMD). The shape
-# is picked per call from WF_TUNE_QPW.
+# Every kernel shape on every case, whatever the default choice for it: the persistent
+# 32-query kernel (one work group per CU walking a list of work items; calls without a mask,
+# causal ones with four query heads per KV head), and the one-item-per-group kernels with
+# 64-query waves (one per SIMD, row sums over the 16-bit weights) and 32-query waves (two per
+# SIMD). The shape is picked per call from WF_TUNE_PERSIST and WF_TUNE_QPW.
 SHAPE_CASES = [c + (m,) for c in CASES for m in (None,)] + [
     ("bf16", 2, 4, 4, 130, 301, 128, False, "bool"),
     ("fp16", 2, 4, 4, 97, 200, 64, False, "half"),
@@ -135,7 +137,15 @@ SHAPE_CASES = [c + (m,) for c in CASES for m in (None,)] + [
 ]
 
 
-@pytest.mark.parametrize("qpw", [64, 32])
+def _pick_shape(monkeypatch, shape):
+    if shape == "persistent":
+        monkeypatch.setenv("WF_TUNE_PERSIST", "1")
+    else:
+        monkeypatch.setenv("WF_TUNE_PERSIST", "0")
+        monkeypatch.setenv("WF_TUNE_QPW", str(shape))
+
+
+@pytest.mark.parametrize("qpw", ["persistent", 64, 32])
 @pytest.mark.parametrize("case", SHAPE_CASES, ids=[str(c) for c in SHAPE_CASES])
 def test_kernel_shapes(case, qpw, monkeypatch):
     dt, B, Hq, Hkv, Lq, Lk, D, causal, mkind = case
@@ -145,9 +155,34 @@ def test_kernel_shapes(case, qpw, monkeypatch):
         w["mask"] = _mask(mkind, "b1", B, Hq, Lq, Lk, w["q"].dtype, g)
     ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w.get("mask"), is_causal=causal,
                          scale=np.float32(w["scale"]))
-    monkeypatch.setenv("WF_TUNE_QPW", str(qpw))
+    _pick_shape(monkeypatch, qpw)
     out = run(w, is_causal=causal)
-    assert_close(out, ref, w["q"].dtype, f"{case} qpw={qpw}")
+    assert_close(out, ref, w["q"].dtype, f"{case} {qpw}")
+
+
+# Calls with more work items than the GPU has CUs, so that the persistent kernel's work
+# groups walk several items each: its K/V copies and Q loads then cross item (and KV-head)
+# boundaries. Both work orders are covered: B*Hkv a multiple of 8 (each XCD keeps its KV
+# groups) and not.
+PERSIST_CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, causal
+    ("bf16", 2, 32, 8, 1100, 1100, 64, True),     # 18 q-tiles x 16 KV groups, XCD order
+    ("fp16", 3, 16, 4, 1500, 1500, 64, True),     # 24 x 12, plain order
+    ("bf16", 4, 16, 16, 1100, 300, 128, False),   # HPW 1: 5 q-tiles x 64 groups
+    ("fp16", 3, 16, 8, 1300, 777, 128, False),    # HPW 2: 11 x 24
+    ("bf16", 2, 32, 8, 777, 2100, 128, True),     # causal with Lq < Lk (top-left)
+]
+
+
+@pytest.mark.parametrize("case", PERSIST_CASES, ids=[str(c) for c in PERSIST_CASES])
+def test_persistent_many_items(case, monkeypatch):
+    dt, B, Hq, Hkv, Lq, Lk, D, causal = case
+    monkeypatch.setenv("WF_TUNE_PERSIST", "1")
+    w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 991)
+    ref, ref_lse = oracle.sdpa(w["q"], w["k"], w["v"], is_causal=causal, scale=np.float32(w["scale"]))
+    out, lse = run(w, is_causal=causal, return_lse=True)
+    assert_close(out, ref, w["q"].dtype, str(case))
+    assert np.abs(to64(lse) - ref_lse).max() < 1e-3
+    assert torch.equal(run(w, is_causal=causal), out)
 
 
 def test_deterministic():
@@ -175,13 +210,13 @@ def _sampled_rows_causal(w, out, picks, rows):
             assert_close(out[b:b + 1, h:h + 1, i0:i1], ref, q.dtype, f"b{b} h{h} rows {i0}:{i1}")
 
 
-@pytest.mark.parametrize("qpw", [None, 64])
+@pytest.mark.parametrize("qpw", [None, 64, 32])
 def test_causal_gqa_prefill_full_size_sampled(qpw, monkeypatch):
     """B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal, in the benchmark's launch configuration
-    (qpw None) and with 64-query waves; sampled rows across the sequence checked against the
-    oracle."""
+    (qpw None) and with the one-item-per-group kernels (64- and 32-query waves); sampled rows
+    across the sequence checked against the oracle."""
     if qpw is not None:
-        monkeypatch.setenv("WF_TUNE_QPW", str(qpw))
+        _pick_shape(monkeypatch, qpw)
     w = causal_gqa_prefill()
     out = run(w, is_causal=True)
     assert tuple(out.shape) == (4, 32, 4096, 128)
