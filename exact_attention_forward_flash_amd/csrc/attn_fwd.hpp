@@ -34,8 +34,9 @@
 namespace wf {
 
 enum { MASK_NONE = 0, MASK_BOOL = 1, MASK_HALF = 2, MASK_F32 = 3 };
-// MODE_DENSE_P tags the table rows of the persistent dense kernel (attn_fwd_p.hpp).
-enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3 };
+// MODE_DENSE_P / MODE_DENSE_P16 tag the table rows of the persistent dense kernel
+// (attn_fwd_p.hpp) with fp32 row sums and with row sums over the 16-bit weights.
+enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3, MODE_DENSE_P16 = 4 };
 
 struct FwdArgs {
   const void* q; const void* q2; const void* k; const void* k2; const void* v;

@@ -31,7 +31,7 @@ namespace wf {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int DQK, int DV, int HPW, bool CAUSAL>
+template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16>
 struct AttnFwdP {
   static constexpr int NW = 8;
   static constexpr int BN = 64;
@@ -127,6 +127,10 @@ struct AttnFwdP {
     const int hw = w / WPH;
     const int qw = (w % WPH) * 32;
     const float c = a.scale_log2;
+    // PRESCALE (calls without the lse): Q carries c (see read_q) and scores come out in log2
+    // units; otherwise they stay in raw units and the weight is exp2(c * (t - m_ref / c)).
+    constexpr bool PRESCALE = SUM16;
+    const float cs = PRESCALE ? 1.0f : c, inv_cs = PRESCALE ? 1.0f : 1.0f / c;
 
     // ---- copies into LDS: buffer loads with a descriptor whose size ends at the first row
     // that must not be read (those rows land as zeros) and a per-lane byte offset that is
@@ -140,39 +144,61 @@ struct AttnFwdP {
       const uint32_t nrec = bytes <= 0 ? 0u : bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
       return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nrec, 0x00020000);
     };
-    uint32_t kvo[KLOADS], vvo[VLOADS], qvo[QLOADS];
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int q = (i * NW + w) * 64 + lane;
-      const int r = q / KCH, pos = q % KCH;
-      kvo[i] = (uint32_t)r * (uint32_t)(a.k_sm * 2) + (uint32_t)((pos ^ kswz(r)) * 16);
+    // The swizzles repeat every KPER rows (K, Q) / 4 rows (V), so copies that start a
+    // multiple of that many rows apart share the per-lane offset; each gets a descriptor of
+    // its own whose base is moved by those rows (and whose size shrinks with it: the range
+    // check covers only the per-lane offset).
+    constexpr int KPER = KCH == 16 ? 16 : 32;
+    constexpr int KROWS = NT / KCH, VROWS = NT / VCH, QROWS = 64 / KCH;  // rows per copy
+    constexpr int QV = KPER / QROWS < QLOADS ? KPER / QROWS : QLOADS;   // distinct Q offsets
+    static_assert(KLOADS == 1 || KROWS % KPER == 0, "K copies share their offsets");
+    static_assert(VLOADS == 1 || VROWS % 4 == 0, "V copies share their offsets");
+    static_assert(QLOADS % QV == 0 && (QROWS * QV) % KPER == 0, "Q copies share their offsets");
+    const uint32_t ksm2 = (uint32_t)(a.k_sm * 2), vsm2 = (uint32_t)(a.v_sm * 2), qsm2 = (uint32_t)(a.q_sm * 2);
+    uint32_t kvo, vvo, qvo[QV];
+    {
+      const int q = w * 64 + lane;
+      kvo = (uint32_t)(q / KCH) * ksm2 + (uint32_t)(((q % KCH) ^ kswz(q / KCH)) * 16);
+      vvo = (uint32_t)(q / VCH) * vsm2 + (uint32_t)(((q % VCH) ^ vswz(q / VCH)) * 16);
     }
 #pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int q = (i * NW + w) * 64 + lane;
-      const int r = q / VCH, pos = q % VCH;
-      vvo[i] = (uint32_t)r * (uint32_t)(a.v_sm * 2) + (uint32_t)((pos ^ vswz(r)) * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < QLOADS; ++i) {
+    for (int i = 0; i < QV; ++i) {
       const int q = i * 64 + lane;
       const int r = q / KCH, pos = q % KCH;
-      qvo[i] = (uint32_t)r * (uint32_t)(a.q_sm * 2) + (uint32_t)((pos ^ kswz(r)) * 16);
+      qvo[i] = (uint32_t)r * qsm2 + (uint32_t)((pos ^ kswz(r)) * 16);
     }
     WF_LDS char* const sQw = sQ + w * QBYTES;
     auto stage_q = [&](const Item& it) {
       const int row0 = it.pos0 + qw;
       const T* base = (const T*)a.q + it.b * a.q_sb + (it.hq0 + hw) * a.q_sh + (int64_t)row0 * a.q_sm;
-      const auto rs = rsrc(base, it.n > 0 ? (int64_t)(a.Lq - row0) * a.q_sm * 2 : 0);
+      const int64_t bytes = it.n > 0 ? (int64_t)(a.Lq - row0) * a.q_sm * 2 : 0;
 #pragma unroll
-      for (int i = 0; i < QLOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (WF_LDS void*)(sQw + i * 1024), 16, (int)qvo[i], 0, 0, 0);
+      for (int i = 0; i < QLOADS; ++i) {
+        const int64_t off = (int64_t)(i / QV) * QV * QROWS * qsm2;
+        const auto rs = rsrc((const char*)base + off, bytes - off);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (WF_LDS void*)(sQw + i * 1024), 16, (int)qvo[i % QV], 0, 0, 0);
+      }
     };
     // Q^T operand from the staging area: lane (j, hf) takes row j, head-dim 16s + 8hf .. +7.
+    // With PRESCALE it is multiplied by c = scale*log2(e) in fp32 and rounded back to the
+    // input type, so that the S^T MFMAs produce log2-domain scores and the weights need no
+    // per-element scaling. That rounding (relative 2^-9 per element for bf16) does not
+    // average out: for a fixed c it shifts all scores of a row by a common factor of order
+    // 1e-4, which moves the log-sum-exp by a few 1e-4 (measured on N(0,1) inputs: output
+    // error up to ~1e-3, as large as the output's own rounding). Calls that ask for the lse
+    // therefore keep Q as it is and scale every score in fp32.
     u32x4 qf[NS];
     auto read_q = [&]() {
+      typedef typename Mfma16<T>::v8 v8;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) qf[s] = lds_read16(sQw + j * KCH * 16 + (((2 * s + hf) ^ kswz(j)) * 16));
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 raw = lds_read16(sQw + j * KCH * 16 + (((2 * s + hf) ^ kswz(j)) * 16));
+        const v8 x = __builtin_bit_cast(v8, raw);
+        v8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = PRESCALE ? (T)((float)x[e] * c) : x[e];
+        qf[s] = __builtin_bit_cast(u32x4, y);
+      }
     };
 
     // A copy cursor walks the tiles of the group's items for one tensor: the item, the tile
@@ -208,19 +234,17 @@ struct AttnFwdP {
         cu.rem -= st;
       }
     };
+    Cursor ck, cv;  // the K copy runs two tiles ahead of the compute, the V copy one
+    // Copy i of the tile the cursor points at.
+    auto issue_one = [&](const Cursor& cu, bool is_v, WF_LDS char* dst, int i) {
+      const int64_t off = (int64_t)i * (is_v ? VROWS * vsm2 : KROWS * ksm2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(cu.base + off, cu.rem - off),
+                                               (WF_LDS void*)(dst + (i * NW + w) * 1024), 16,
+                                               (int)(is_v ? vvo : kvo), 0, 0, 0);
+    };
     auto issue = [&](const Cursor& cu, bool is_v, WF_LDS char* dst) {
-      const auto rs = rsrc(cu.base, cu.rem);
-      if (!is_v) {
 #pragma unroll
-        for (int i = 0; i < KLOADS; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (WF_LDS void*)(dst + (i * NW + w) * 1024), 16,
-                                                   (int)kvo[i], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < VLOADS; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (WF_LDS void*)(dst + (i * NW + w) * 1024), 16,
-                                                   (int)vvo[i], 0, 0, 0);
-      }
+      for (int i = 0; i < (is_v ? VLOADS : KLOADS); ++i) issue_one(cu, is_v, dst, i);
     };
 
     // ---- LDS operand offsets (as in attn_fwd.hpp) ----
@@ -270,15 +294,29 @@ struct AttnFwdP {
     for (int n = 0; n < NDV; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    const f32x16 zero = {};
+    // Softmax state (per lane: its query row), in log2 units. m_run is the reference max
+    // (-inf before the item's first tile), l_run the sum of the weights. The S^T accumulators
+    // start from -m_ref (over c without PRESCALE) instead of 0, so a tile comes out relative
+    // to m_ref and its weights need no subtraction; m_ref is the reference the pending tile
+    // was computed against (m_run, or 0 while m_run is -inf). The start value is rebuilt for
+    // every tile (16 moves) rather than kept in 16 registers.
+    float m_run = -INFINITY, l_run = 0.f, m_ref = 0.f;
+    auto acc_start = [&]() {
+      float v = -m_ref * inv_cs;
+      asm volatile("" : "+v"(v));  // not hoisted out of the loop
+      f32x16 r16;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) r16[r] = v;
+      return r16;
+    };
 
     auto s_tile = [&](const WF_LDS char* Kt, f32x16* sc) {
+      const f32x16 mref16 = acc_start();
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const u32x4 k0f = kfrag(Kt, s, 0), k1f = kfrag(Kt, s, 1);
-        sc[0] = Mfma16<T>::run(k0f, qf[s], s == 0 ? zero : sc[0]);
-        sc[1] = Mfma16<T>::run(k1f, qf[s], s == 0 ? zero : sc[1]);
+        sc[0] = Mfma16<T>::run(k0f, qf[s], s == 0 ? mref16 : sc[0]);
+        sc[1] = Mfma16<T>::run(k1f, qf[s], s == 0 ? mref16 : sc[1]);
       }
     };
     auto tile_max = [&](const f32x16* sc) {
@@ -287,32 +325,47 @@ struct AttnFwdP {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      return xhalf_max(mx) * c;
+      return xhalf_max(mx) * cs;
     };
-    auto rescale = [&](float mt) {
-      if (wave_any(mt > m_run + 8.0f)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+    // mt: max of the current tile relative to m_ref. The reference max moves (O and l
+    // rescaled, the tile shifted onto the new reference) only when some query's tile max
+    // passes it by more than 8, so p = exp2(t - m) stays <= 2^8.
+    auto rescale = [&](float mt, f32x16* cur) {
+      const float m_abs = m_ref + mt;
+      if (wave_any(m_abs > m_run + 8.0f)) {
+        const float m_new = fmaxf(m_run, m_abs);
+        const float m_new_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_new_ref);
         l_run *= alpha;
 #pragma unroll
         for (int n = 0; n < NDV; ++n)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
+        const float d = m_new_ref - m_ref;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) cur[kb][r] -= d * inv_cs;
         m_run = m_new;
+        m_ref = m_new_ref;
       }
     };
 
     f32x16 sc[2], sn[2];
     u32x4 pk[4];
-    u32x4 vq[2][NDV];   // V^T operands, two PV steps ahead
+    u32x4 vq[NDV];   // V^T operands of the next PV step
     float mt_cur = -INFINITY;
 
     // Phase A: the next tile's S^T MFMAs with the current tile's exponentials between them.
     // K operands run two steps ahead; near the end the V^T operands of the first PV step
     // are read (the V tile landed in the previous iteration).
-    auto phase_a = [&](const WF_LDS char* Kn, const WF_LDS char* Vc, f32x16* cur, f32x16* nxt) {
+    // A wave in this phase issues ahead of one in phase B (s_setprio): measured to keep the
+    // MFMA pipe busier than equal priorities.
+    auto phase_a = [&](const WF_LDS char* Kn, const WF_LDS char* Vc, f32x16* cur, f32x16* nxt,
+                       WF_LDS char* Kfill) {
+      __builtin_amdgcn_s_setprio(3);
       constexpr int EPS = 32 / NS;  // exponentials per step
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      const f32x16 mref16 = acc_start();
       u32x4 kp[2][2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -327,46 +380,49 @@ struct AttnFwdP {
           kp[s & 1][0] = kfrag(Kn, s + 2, 0);
           kp[s & 1][1] = kfrag(Kn, s + 2, 1);
         }
-        nxt[0] = Mfma16<T>::run(a0, qf[s], s == 0 ? zero : nxt[0]);
+        nxt[0] = Mfma16<T>::run(a0, qf[s], s == 0 ? mref16 : nxt[0]);
 #pragma unroll
         for (int e = s * EPS; e < s * EPS + EPS / 2; ++e) {
-          const float pe = fast_exp2(fmaf(cur[e >> 4][e & 15], c, neg_m));
+          const float pe = fast_exp2(PRESCALE ? cur[e >> 4][e & 15] : cur[e >> 4][e & 15] * cs);
           cur[e >> 4][e & 15] = pe;
-          ps[0] += pe;
+          if (!SUM16) ps[0] += pe;
         }
-        nxt[1] = Mfma16<T>::run(a1, qf[s], s == 0 ? zero : nxt[1]);
+        nxt[1] = Mfma16<T>::run(a1, qf[s], s == 0 ? mref16 : nxt[1]);
 #pragma unroll
         for (int e = s * EPS + EPS / 2; e < (s + 1) * EPS; ++e) {
-          const float pe = fast_exp2(fmaf(cur[e >> 4][e & 15], c, neg_m));
+          const float pe = fast_exp2(PRESCALE ? cur[e >> 4][e & 15] : cur[e >> 4][e & 15] * cs);
           cur[e >> 4][e & 15] = pe;
-          ps[1] += pe;
+          if (!SUM16) ps[1] += pe;
         }
         if (s == NS - 2) {
 #pragma unroll
-          for (int n = 0; n < NDV; ++n) vq[0][n] = vfrag(Vc, 0, n);
+          for (int n = 0; n < NDV; ++n) vq[n] = vfrag(Vc, 0, n);
         }
+#pragma unroll
+        for (int i = 0; i < KLOADS; ++i)
+          if (s == (2 * i + 1) * NS / (2 * KLOADS)) issue_one(ck, false, Kfill, i);
       }
-      l_run += ps[0] + ps[1];
+      if (!SUM16) l_run += ps[0] + ps[1];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         pk[m] = pack8<T>(cur[m >> 1], 8 * (m & 1));
         // keeps the exponentials here, among the S^T MFMAs, rather than sunk to their uses
         asm volatile("" ::"v"(pk[m]));
       }
+      __builtin_amdgcn_s_setprio(0);
     };
-    // Phase B: O^T += V^T P^T for the current tile (V^T operands two steps ahead), with the
+    // Phase B: O^T += V^T P^T for the current tile (V^T operands one step ahead), with the
     // next tile's row max in between.
-    auto phase_b = [&](const WF_LDS char* Vc, const f32x16* nxt) {
-#pragma unroll
-      for (int n = 0; n < NDV; ++n) vq[1][n] = vfrag(Vc, 1, n);
+    auto phase_b = [&](const WF_LDS char* Vc, const f32x16* nxt, WF_LDS char* Vfill) {
       float mx[2] = {-INFINITY, -INFINITY};
+      float lp[2] = {0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         u32x4 va[NDV];
 #pragma unroll
         for (int n = 0; n < NDV; ++n) {
-          va[n] = vq[m & 1][n];
-          if (m + 2 < 4) vq[m & 1][n] = vfrag(Vc, m + 2, n);
+          va[n] = vq[n];
+          if (m + 1 < 4) vq[n] = vfrag(Vc, m + 1, n);
         }
 #pragma unroll
         for (int n = 0; n < NDV; ++n) {
@@ -375,8 +431,17 @@ struct AttnFwdP {
           for (int e = 8 * m + 2 * n; e < 8 * m + 2 * n + 2; ++e)
             mx[n & 1] = fmaxf(mx[n & 1], nxt[e >> 4][e & 15]);
         }
+        if (SUM16) lp[m & 1] = sum8_acc<T>(pk[m], lp[m & 1]);
+#pragma unroll
+        for (int i = 0; i < VLOADS; ++i)
+          if (m == i * 4 / VLOADS) issue_one(cv, true, Vfill, i);
       }
-      mt_cur = xhalf_max(fmaxf(mx[0], mx[1])) * c;
+      if (SUM16) {
+        // 3 wait states between the last v_dot2c write and an ordinary VALU read of it.
+        asm volatile("s_nop 2" : "+v"(lp[0]), "+v"(lp[1]));
+        l_run += lp[0] + lp[1];
+      }
+      mt_cur = xhalf_max(fmaxf(mx[0], mx[1])) * cs;
     };
 
     // Output of an item: O / l, rows past Lq dropped; the log-sum-exp when asked for.
@@ -409,7 +474,6 @@ struct AttnFwdP {
     if (cur_it.n == 0) return;
     Item nxt_it = item_at(list, 1);
     stage_q(cur_it);
-    Cursor ck, cv;
     enter(ck, 0, false);
     enter(cv, 0, true);
     issue(ck, false, sK0);
@@ -438,22 +502,20 @@ struct AttnFwdP {
     bool done = false;
     auto iter = [&](const WF_LDS char* Kn, WF_LDS char* Kfill, const WF_LDS char* Vc,
                     WF_LDS char* Vfill, f32x16* cur, f32x16* nxt) {
-      issue(ck, false, Kfill);
-      advance(ck, false);
-      issue(cv, true, Vfill);
-      advance(cv, true);
       const bool last = u + 1 == cur_it.n;
       if (last) {
         read_q();
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         stage_q(item_at(list, cur_it.k + 2));
       }
-      rescale(mt_cur);
-      phase_a(Kn, Vc, cur, nxt);
+      rescale(mt_cur, cur);
+      phase_a(Kn, Vc, cur, nxt, Kfill);   // copies K_{g+2} into Kfill on the way
       const int kt_n = last ? 0 : u + 1;
       const int pos_n = last ? nxt_it.pos0 : cur_it.pos0;
       if (need_mask(kt_n, pos_n)) apply_mask(kt_n, pos_n, nxt);
-      phase_b(Vc, nxt);
+      phase_b(Vc, nxt, Vfill);            // copies V_{g+1} into Vfill on the way
+      advance(ck, false);
+      advance(cv, true);
       wait_vmem();
       __syncthreads();
       if (last) {
@@ -462,7 +524,7 @@ struct AttnFwdP {
         for (int n = 0; n < NDV; ++n)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
-        m_run = -INFINITY;
+        m_run = -INFINITY;   // m_ref stays: the next item's first tile was computed against it
         l_run = 0.f;
         cur_it = nxt_it;
         nxt_it = item_at(list, cur_it.k + 1);
@@ -482,14 +544,18 @@ struct AttnFwdP {
   }
 };
 
-template <typename T, int DQK, int DV, int HPW, bool CAUSAL>
+template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_p_kernel(FwdArgs a) {
-  typedef AttnFwdP<T, DQK, DV, HPW, CAUSAL> K;
-  __shared__ __attribute__((aligned(1024))) char sK0[K::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[K::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[K::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[K::VBYTES];
+  typedef AttnFwdP<T, DQK, DV, HPW, CAUSAL, SUM16> K;
+  // Separate LDS arrays, so that the compiler can tell a tile copy into one buffer from the
+  // operand reads of another and does not wait for the copy before them. The tile buffers
+  // carry the largest alignment, which places them first: every operand read in the tile loop
+  // then addresses them as a per-lane offset plus an immediate (< 64 KiB).
+  __shared__ __attribute__((aligned(16384))) char sK0[K::KBYTES];
+  __shared__ __attribute__((aligned(16384))) char sK1[K::KBYTES];
+  __shared__ __attribute__((aligned(16384))) char sV0[K::VBYTES];
+  __shared__ __attribute__((aligned(16384))) char sV1[K::VBYTES];
   __shared__ __attribute__((aligned(1024))) char sQ[K::NW * K::QBYTES];
   __shared__ __attribute__((aligned(16))) i32x4 list[K::MAX_ITEMS];
   K::run(a, (WF_LDS char*)sK0, (WF_LDS char*)sK1, (WF_LDS char*)sV0, (WF_LDS char*)sV1,

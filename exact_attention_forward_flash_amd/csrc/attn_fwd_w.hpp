@@ -61,26 +61,6 @@ __device__ __forceinline__ void o_settle(f32x16 (&o)[2][4]) {
                  "+a"(o[1][1]), "+a"(o[1][2]), "+a"(o[1][3]));
 }
 
-// Sum of the 8 16-bit values packed in x, accumulated into acc (fp32): v_dot2c with (1, 1).
-// Written out because the compiler's fdot2 builtins, applied to the elements of a vector in
-// turn, were seen to read the first element for all of them. A dot2c result may feed the
-// next dot2c's accumulator at once, but an ordinary VALU read of it needs 3 wait states
-// first (the caller issues them).
-template <typename T>
-__device__ __forceinline__ float sum8_acc(u32x4 x, float acc);
-template <>
-__device__ __forceinline__ float sum8_acc<__bf16>(u32x4 x, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(x[i]));
-  return acc;
-}
-template <>
-__device__ __forceinline__ float sum8_acc<_Float16>(u32x4 x, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) asm("v_dot2c_f32_f16 %0, 0x3c003c00, %1" : "+v"(acc) : "v"(x[i]));
-  return acc;
-}
-
 template <typename T, int DQK, int DQK1, int DV, int HPW, int MASK, bool CAUSAL, int MODE>
 struct AttnFwdW {
   static constexpr int NW = 4;   // one wave per SIMD

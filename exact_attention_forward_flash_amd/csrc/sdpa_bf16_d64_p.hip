@@ -2,8 +2,12 @@
 #include "wf_internal.hpp"
 
 namespace wf {
-#define E(HPW, CAUSAL) WF_ATTN_P_ENTRY(__bf16, DT_BF16, 64, HPW, CAUSAL)
-static const AttnEntry kTable[] = {E(1, false), E(2, false), E(4, false), E(4, true)};
+#define E(HPW, CAUSAL, SUM16) WF_ATTN_P_ENTRY(__bf16, DT_BF16, 64, HPW, CAUSAL, SUM16)
+// SUM16: row sums over the 16-bit weights (calls without the lse), else fp32 sums.
+static const AttnEntry kTable[] = {
+    E(1, false, true),  E(2, false, true),  E(4, false, true),  E(4, true, true),
+    E(1, false, false), E(2, false, false), E(4, false, false), E(4, true, false),
+};
 #undef E
 const AttnEntry* attn_table_p_bf16_d64(int* n) {
   *n = (int)(sizeof(kTable) / sizeof(kTable[0]));

@@ -235,7 +235,10 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   bool persist = mask_kind == wf::MASK_NONE && Lk > 0 && w64_ok && q_ok && (!causal || hpw == 4);
   if (const char* t = getenv("WF_TUNE_PERSIST")) persist = persist && atoi(t) != 0;
   if (persist) {
-    const wf::AttnEntry* pe = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, wf::MASK_NONE, causal, wf::MODE_DENSE_P);
+    // Without the lse the row sums are taken over the 16-bit weights (exactly the weights
+    // that multiply V; their sum keeps the 16-bit rounding, which the lse would show).
+    const int pmode = lse == nullptr ? wf::MODE_DENSE_P16 : wf::MODE_DENSE_P;
+    const wf::AttnEntry* pe = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, wf::MASK_NONE, causal, pmode);
     const int ncu = cu_count();
     if (pe != nullptr && ncu > 0) {
       a.n_qtiles = (Lq + pe->bmp - 1) / pe->bmp;

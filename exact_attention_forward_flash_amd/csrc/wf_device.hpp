@@ -86,6 +86,26 @@ __device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballo
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum of the 8 16-bit values packed in x, accumulated into acc (fp32): v_dot2c with (1, 1).
+// Written out because the compiler's fdot2 builtins, applied to the elements of a vector in
+// turn, were seen to read the first element for all of them. A dot2c result may feed the
+// next dot2c's accumulator at once, but an ordinary VALU read of it needs 3 wait states
+// first (the caller issues them).
+template <typename T>
+__device__ __forceinline__ float sum8_acc(u32x4 x, float acc);
+template <>
+__device__ __forceinline__ float sum8_acc<__bf16>(u32x4 x, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm("v_dot2c_f32_bf16 %0, 0x3f803f80, %1" : "+v"(acc) : "v"(x[i]));
+  return acc;
+}
+template <>
+__device__ __forceinline__ float sum8_acc<_Float16>(u32x4 x, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm("v_dot2c_f32_f16 %0, 0x3c003c00, %1" : "+v"(acc) : "v"(x[i]));
+  return acc;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

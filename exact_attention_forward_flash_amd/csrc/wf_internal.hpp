@@ -50,10 +50,11 @@ const AttnEntry* attn_table_p_f16_d64(int* n);
 
 // Persistent dense kernel (32 queries per wave, 8 waves, no mask): one work group per CU
 // walks its list of at most AttnFwdP<...>::MAX_ITEMS work items.
-#define WF_ATTN_P_ENTRY(T, DT, D, HPW, CAUSAL)                                               \
-  {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL, MODE_DENSE_P,                                \
-   (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL>, AttnFwdP<T, D, D, HPW, CAUSAL>::BMP, 64}
-constexpr int kPersistMaxItems = AttnFwdP<__bf16, 128, 128, 4, false>::MAX_ITEMS;
+#define WF_ATTN_P_ENTRY(T, DT, D, HPW, CAUSAL, SUM16)                                        \
+  {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL, SUM16 ? MODE_DENSE_P16 : MODE_DENSE_P,      \
+   (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL, SUM16>,                             \
+   AttnFwdP<T, D, D, HPW, CAUSAL, SUM16>::BMP, 64}
+constexpr int kPersistMaxItems = AttnFwdP<__bf16, 128, 128, 4, false, false>::MAX_ITEMS;
 
 // fp32 path (MFMA 32x32x2 f32).
 struct F32Entry {

@@ -1,5 +1,6 @@
-"""The 64-query-wave kernel's inline-asm MFMA / v_dot2c wait states, checked on the code the
-compiler generates for gfx950 (no GPU needed), and the checker itself on planted cases."""
+"""The inline-asm MFMA / v_dot2c wait states of the 64-query-wave and persistent kernels, checked
+on the code the compiler generates for gfx950 (no GPU needed), and the checker itself on planted
+cases."""
 import os
 import shutil
 import subprocess
@@ -35,14 +36,16 @@ def test_checker_finds_planted_hazards():
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-def test_generated_code_has_no_inline_asm_hazards(tmp_path):
+@pytest.mark.parametrize("src_name, kernel", [("sdpa_bf16_d128_w64.hip", "attn_fwd_w_kernel"),
+                                              ("sdpa_bf16_d128_p.hip", "attn_fwd_p_kernel")])
+def test_generated_code_has_no_inline_asm_hazards(tmp_path, src_name, kernel):
     from exact_attention_forward_flash_amd.build import HIPCC, flags_for, CSRC
-    src = os.path.join(CSRC, "sdpa_bf16_d128_w64.hip")
+    src = os.path.join(CSRC, src_name)
     out = tmp_path / "k.s"
     cmd = [HIPCC, *flags_for(src), "--cuda-device-only", "-S", src, "-o", str(out)]
     subprocess.run([c for c in cmd if c != "-fPIC"], check=True, capture_output=True)
     res = check_asm(out.read_text())
-    kernels = [k for k in res if "attn_fwd_w_kernel" in k]
-    assert kernels, "no 64-query-wave kernel in the listing"
+    kernels = [k for k in res if kernel in k]
+    assert kernels, f"no {kernel} in the listing"
     for k in kernels:
         assert not res[k], (k, res[k][:5])
