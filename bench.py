@@ -113,6 +113,103 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(rec))
 
 
+def _time_steps(step, steps, warmup, stream):
+    """Average milliseconds of step() over `steps` runs after `warmup`, from HIP events on the
+    launch stream."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+
+def other_workload(name, steps, warmup):
+    """Times one of the other configurations (parity cases, not the headline line): one JSON
+    line with its kernel throughput. TFLOP/s use 2*Hq*Lq*Lk*(Dqk+Dv) per (batch, sequence),
+    halved for causal; the cache stream also reports the cache update's HBM GB/s (bytes the
+    update reads plus writes)."""
+    import torch
+    import exact_attention_forward_flash_amd as wf
+    import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    line = {"workload": name, "desc": synth.WORKLOADS[name]["desc"], "steps": steps, "warmup": warmup}
+    if name in ("masked_bool", "masked_float"):
+        w = synth.masked_sdpa_inputs(name.split("_")[1])
+        q, k, v, m = (w[n].to(dev) for n in ("q", "k", "v", "mask"))
+        ms = _time_steps(lambda: wf.sdpa(q, k, v, attn_mask=m, scale=w["scale"]), steps, warmup, stream)
+        B, H, L, D = q.shape
+        fl = 4.0 * B * H * L * L * D
+        line.update(ms=round(ms, 4), tflops=round(fl / ms / 1e9, 2))
+    elif name == "varlen_mla":
+        w = synth.varlen_mla_prefill_inputs()
+        t = {n: w[n].to(dev) for n in ("q", "q_rope", "k", "k_rope", "v", "q_seqlen", "kv_seqlen")}
+        ws = torch.empty(max(256, wf.varlen_mla_prefill_workspace_size(16, t["q"].shape[0], 16)),
+                         dtype=torch.uint8, device=dev)
+        ms = _time_steps(lambda: wf.varlen_mla_prefill(
+            t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], t["q_seqlen"], t["kv_seqlen"],
+            w["head_num"], w["kv_head_num"], w["qk_scale"], 1, ws), steps, warmup, stream)
+        lens = [int(x) for x in w["q_seqlen"]]
+        fl = sum(2.0 * w["head_num"] * L * L * (192 + 128) / 2 for L in lens)
+        line.update(ms=round(ms, 4), tflops=round(fl / ms / 1e9, 2), tokens=sum(lens))
+    elif name == "page_example":
+        w = synth.page_example_fp32()
+        q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
+        ms = _time_steps(lambda: wf.sdpa(q, k, v, scale=w["scale"]), steps, warmup, stream)
+        line.update(ms=round(ms, 4), note="launch-latency bound")
+    elif name == "cache_stream":
+        B, H, D, C, sink, window, n = 1, 24, 128, 256, 256, 3840, 64
+        chunks = [(c, q.to(dev), k.to(dev), v.to(dev)) for c, q, k, v in
+                  synth.cache_stream_chunks(B, H, D, C, sink, window, n)]
+        ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+        def run_stream(evs, att_fl):
+            cache = wf.BlockKVCache((B, H, sink + window, D), (B, H, sink + window, D), 2, C,
+                                    window, sink, device=dev)
+            for c, q, k, v in chunks:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                cache.before_update(c)
+                e[0].record(stream)
+                cache.update(k, v)
+                e[1].record(stream)
+                cache.after_update(c)
+                cache.attend(q, workspace=ws)
+                e[2].record(stream)
+                nv, _ = cache.visible()
+                evs.append(e)
+                att_fl.append(4.0 * B * H * C * nv * D)
+            return cache
+
+        for _ in range(max(1, warmup // 10)):
+            run_stream([], [])
+        torch.cuda.synchronize()
+        tot_u = tot_a = 0.0
+        fl = 0.0
+        reps = max(1, steps // 20)
+        for _ in range(reps):
+            evs, afl = [], []
+            run_stream(evs, afl)
+            torch.cuda.synchronize()
+            tot_u += sum(e[0].elapsed_time(e[1]) for e in evs)
+            tot_a += sum(e[1].elapsed_time(e[2]) for e in evs)
+            fl += sum(afl)
+        upd_bytes = 2 * (2 * B * H * C * D * 2) * n  # K and V rows read + written, fp16
+        line.update(chunks=n, streams=reps, update_ms_per_chunk=round(tot_u / reps / n, 4),
+                    update_gbs=round(upd_bytes * reps / (tot_u * 1e-3) / 1e9, 1),
+                    attend_ms_per_chunk=round(tot_a / reps / n, 4),
+                    attend_tflops=round(fl / (tot_a * 1e-3) / 1e12, 2))
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +218,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="causal_gqa",
+                    choices=["causal_gqa", "varlen_mla", "masked_bool", "masked_float",
+                             "cache_stream", "page_example"],
+                    help="causal_gqa (default) prints the headline line; the others time one of "
+                         "the other configurations and print its kernel throughput")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter CSVs "
                          "from rocprofv3 --pmc: record HBM bytes per launch and exit")
@@ -140,6 +242,9 @@ def main():
     import exact_attention_forward_flash_amd as wf
     from synth import causal_gqa_prefill
 
+    if args.workload != "causal_gqa":
+        other_workload(args.workload, args.steps, args.warmup)
+        return
     if args.copy_calibration:
         n = 256 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")

@@ -51,6 +51,7 @@ struct FwdArgs {
   int causal_shift;   // key j kept for query i iff j <= i + shift
   int n_qtiles;       // query tiles per head group (dense / split)
   int mask_vec;       // mask rows allow 4-element vector loads
+  int mask_lds;       // bool / 16-bit mask tiles may be copied into LDS (16-byte aligned rows)
   float scale_log2;   // scale * log2(e)
   float inv_scale;    // 1 / scale (float masks are added to raw scores as mask / scale)
   // varlen (persistent) mode
@@ -95,6 +96,18 @@ struct AttnFwd {
   static constexpr int VBYTES = BN * DV * 2;
   static constexpr int NS = DQK / 16;
   static constexpr int NDV = DV / 32;
+  // Bool and 16-bit masks of one-head groups: the mask tile of the group's rows (BMP rows x BN
+  // keys) is copied into LDS with the K tile (coalesced), instead of every lane reading its own
+  // row from global memory (32 rows per load instruction).
+  static constexpr int MSZ = MASK == MASK_BOOL ? 1 : MASK == MASK_HALF ? 2 : 4;
+  static constexpr bool MLDS = (MASK == MASK_BOOL || MASK == MASK_HALF) && HPW == 1 && MODE == MODE_DENSE;
+  static constexpr int MROWB = BN * MSZ;                 // bytes of one row of a mask tile
+  static constexpr int MBYTES = MLDS ? BMP * MROWB : 16;
+  static constexpr int MLOADS = MLDS ? MBYTES / (NT * 16) : 0;
+  static_assert(!MLDS || MBYTES % (NT * 16) == 0, "mask tile copies split evenly");
+  // K and V tiles of 16 KiB carry the largest alignment, which places them first in LDS
+  // (operand reads then address them with immediate offsets).
+  static constexpr int KALIGN = (KBYTES == 16384 && VBYTES == 16384) ? 16384 : 1024;
   static_assert(sizeof(T) == 2, "16-bit inputs only");
   static_assert(NW % HPW == 0, "waves split evenly over heads");
   static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile copies split evenly");
@@ -115,7 +128,8 @@ struct AttnFwd {
 
   static __device__ __forceinline__ void run(const FwdArgs& a, const WorkItem& it,
                                              WF_LDS char* sK0, WF_LDS char* sK1,
-                                             WF_LDS char* sV0, WF_LDS char* sV1) {
+                                             WF_LDS char* sV0, WF_LDS char* sV1,
+                                             WF_LDS char* sM0, WF_LDS char* sM1) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 31, hf = lane >> 5;
@@ -190,6 +204,39 @@ struct AttnFwd {
       }
     };
 
+    // Mask tile copies (MLDS): buffer loads with a per-tile descriptor ending after the last
+    // valid row's keys; copy i of wave w fills chunks [(i*NW + w)*64, +64) of the tile, lane
+    // -> chunk c, row c / (MROWB/16), byte 16 * (c % (MROWB/16)) of the row.
+    uint32_t mvo[MLOADS > 0 ? MLOADS : 1];
+    const char* mtile0 = nullptr;
+    int64_t mrows_bytes = 0;
+    if constexpr (MLDS) {
+      const int64_t rs = a.mk_sm * MSZ;
+#pragma unroll
+      for (int i = 0; i < MLOADS; ++i) {
+        const int c = (i * NW + w) * 64 + lane;
+        mvo[i] = (uint32_t)(c / (MROWB / 16)) * (uint32_t)rs + (uint32_t)(16 * (c % (MROWB / 16)));
+      }
+      mtile0 = (const char*)a.mask + (it.b * a.mk_sb + it.hq0 * a.mk_sh + (int64_t)it.pos0 * a.mk_sm) * MSZ;
+      const int rows = it.Lq - it.pos0 < BMP ? it.Lq - it.pos0 : BMP;
+      mrows_bytes = (int64_t)(rows - 1) * rs;
+    }
+    auto issue_m = [&](int kt, WF_LDS char* Mt) {
+      if constexpr (MLDS) {
+        if (a.mask_lds) {
+          const int k0 = kt * BN;
+          const int64_t keys = it.Lk - k0 < BN ? it.Lk - k0 : BN;
+          const int64_t bytes = mrows_bytes + keys * MSZ;
+          const uint32_t nrec = bytes <= 0 ? 0u : bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes;
+          const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(mtile0 + (int64_t)k0 * MSZ), 0, (int)nrec, 0x00020000);
+#pragma unroll
+          for (int i = 0; i < MLOADS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (WF_LDS void*)(Mt + (i * NW + w) * 1024), 16,
+                                                     (int)mvo[i], 0, 0, 0);
+        }
+      }
+    };
+
     // ---- LDS operand offsets ----------------------------------------------------------
     // K operand (A of S^T): lane (j, hf) reads key row 32kb + j, chunk 2s + hf
     // (swizzle(32kb + j) == swizzle(j)).
@@ -257,12 +304,28 @@ struct AttnFwd {
       float mval[2][4][4];
       if constexpr (MASK != MASK_NONE) {
         const bool vec = a.mask_vec && (k0 + BN <= it.Lk);
+        const bool lds = MLDS && a.mask_lds;
+        const WF_LDS char* mt = ((kt - it.kt_lo) & 1) ? sM1 : sM0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int key = k0 + 32 * kb + 8 * q4 + 4 * hf;
-            if (vec) {
+            if (lds) {
+              // this lane's row of the tile (qw + j), keys 32kb + 8q4 + 4hf .. +3
+              const WF_LDS char* src = mt + (qw + j) * MROWB + (32 * kb + 8 * q4 + 4 * hf) * MSZ;
+              if constexpr (MASK == MASK_BOOL) {
+                const uint32_t bits = *reinterpret_cast<const WF_LDS uint32_t*>(src);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  mval[kb][q4][e] = ((bits >> (8 * e)) & 0xffu) ? 0.f : -INFINITY;
+              } else if constexpr (MASK == MASK_HALF) {
+                typedef T t4 __attribute__((ext_vector_type(4)));
+                const t4 hv = *reinterpret_cast<const WF_LDS t4*>(src);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = (float)hv[e];
+              }
+            } else if (vec) {
               if constexpr (MASK == MASK_BOOL) {
                 const uint32_t bits = *reinterpret_cast<const uint32_t*>(mrow + key);
 #pragma unroll
@@ -423,8 +486,12 @@ struct AttnFwd {
     const int n_live = kt_live - it.kt_lo;
     if (n_tiles > 0) {
       issue_k(it.kt_lo, sK0);
+      issue_m(it.kt_lo, sM0);
       issue_v(it.kt_lo, sV0);
-      if (n_tiles > 1) issue_k(it.kt_lo + 1, sK1);
+      if (n_tiles > 1) {
+        issue_k(it.kt_lo + 1, sK1);
+        issue_m(it.kt_lo + 1, sM1);
+      }
       wait_vmem();
       __syncthreads();
       if (n_live > 0) {
@@ -435,7 +502,10 @@ struct AttnFwd {
       __syncthreads();  // K_0's buffer is refilled by the first iteration
       auto iter = [&](int u, const WF_LDS char* Kn, WF_LDS char* Kfill, const WF_LDS char* Vc,
                       WF_LDS char* Vfill, f32x16* cur, f32x16* nxt) {
-        if (u + 2 < n_tiles) issue_k(it.kt_lo + u + 2, Kfill);
+        if (u + 2 < n_tiles) {
+          issue_k(it.kt_lo + u + 2, Kfill);
+          issue_m(it.kt_lo + u + 2, (u & 1) ? sM1 : sM0);   // mask tile u+2 replaces tile u's
+        }
         if (u + 1 < n_tiles) issue_v(it.kt_lo + u + 1, Vfill);
         if (u < n_live) {
           // The next tile's S^T and row max are always computed: on this wave's last live
@@ -587,12 +657,15 @@ template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdArgs a) {
   typedef AttnFwd<T, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE> K;
-  __shared__ __attribute__((aligned(1024))) char sK0[K::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[K::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[K::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[K::VBYTES];
+  __shared__ __attribute__((aligned(K::KALIGN))) char sK0[K::KBYTES];
+  __shared__ __attribute__((aligned(K::KALIGN))) char sK1[K::KBYTES];
+  __shared__ __attribute__((aligned(K::KALIGN))) char sV0[K::VBYTES];
+  __shared__ __attribute__((aligned(K::KALIGN))) char sV1[K::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sM0[K::MBYTES];
+  __shared__ __attribute__((aligned(1024))) char sM1[K::MBYTES];
   attn_dispatch<K, MODE, CAUSAL>(a, [&](const WorkItem& it) {
-    K::run(a, it, (WF_LDS char*)sK0, (WF_LDS char*)sK1, (WF_LDS char*)sV0, (WF_LDS char*)sV1);
+    K::run(a, it, (WF_LDS char*)sK0, (WF_LDS char*)sK1, (WF_LDS char*)sV0, (WF_LDS char*)sV1,
+           (WF_LDS char*)sM0, (WF_LDS char*)sM1);
   });
 }
 

@@ -187,7 +187,7 @@ int resolve_scale(float scale, int64_t dqk, float* out) {
 // Dense attention over already validated operands (shared by SDPA and the cache attend when
 // a single split suffices). mask_kind: wf::MASK_*.
 int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const wf_tensor* mask,
-              int mask_kind, bool mask_vec, int causal, float scale, wf_tensor* out, float* lse,
+              int mask_kind, bool mask_vec, bool mask_lds, int causal, float scale, wf_tensor* out, float* lse,
               int64_t Lk, hipStream_t stream) {
   const int B = (int)q->shape[0], Hq = (int)q->shape[1], Lq = (int)q->shape[2];
   const int Dqk = (int)q->shape[3], Hkv = (int)k->shape[1], Dv = (int)v->shape[3];
@@ -206,6 +206,7 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.Lq = Lq; a.Lk = (int)Lk;
   a.causal_shift = 0;
   a.mask_vec = mask_vec ? 1 : 0;
+  a.mask_lds = mask_lds ? 1 : 0;
   a.scale_log2 = scale * wf::kLog2e;
   a.inv_scale = 1.0f / scale;
   const int dt = kernel_dtype(q->dtype);
@@ -248,7 +249,8 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
         return hip_status(launch(pe->fn, dim3((unsigned)P), dim3(512), a, stream), "attention launch");
     }
   }
-  int qpw = (lse == nullptr && !causal && w64_ok) ? 64 : 32;
+  // Masked calls take the 32-query kernel, which copies bool / 16-bit mask tiles into LDS.
+  int qpw = (lse == nullptr && !causal && w64_ok && !(mask_lds && mask_kind != wf::MASK_NONE)) ? 64 : 32;
   if (const char* t = getenv("WF_TUNE_QPW")) qpw = atoi(t) == 32 ? 32 : (atoi(t) == 64 && w64_ok) ? 64 : qpw;
   const wf::AttnEntry* e = nullptr;
   if (qpw == 64) e = find_attn(dt, Dqk, Dqk, Dv, 4, hpw, mask_kind, causal, wf::MODE_DENSE, 64);
@@ -346,7 +348,7 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
   if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(WF_ERR_LAYOUT, "lse must be 4-byte aligned");
   int mask_kind = wf::MASK_NONE;
-  bool mask_vec = false;
+  bool mask_vec = false, mask_lds = false;
   if (mask) {
     if (mask->ndim != 4) return fail(WF_ERR_SHAPE, "mask must be 4-d [B|1, Hq|1, Lq, Lk]");
     const int64_t want[4] = {B, Hq, Lq, Lk};
@@ -367,11 +369,17 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
       mask_vec = reinterpret_cast<uintptr_t>(mask->data) % (4 * ms) == 0;
       for (int i = 0; i < 3; ++i)
         if (mask->shape[i] > 1 && mask->stride[i] % 4 != 0) mask_vec = false;
+      // Bool / 16-bit mask tiles can be copied into LDS when every row starts 16-byte aligned
+      // and 256 rows span less than 2 GiB (32-bit per-lane copy offsets).
+      mask_lds = mask_kind != wf::MASK_F32 && reinterpret_cast<uintptr_t>(mask->data) % 16 == 0 &&
+                 mask->stride[2] >= 0 && mask->stride[2] * ms * 256 < ((int64_t)1 << 31);
+      for (int i = 0; i < 3; ++i)
+        if (mask->shape[i] > 1 && (mask->stride[i] * ms) % 16 != 0) mask_lds = false;
     }
   }
   if (B * Hq * Lq == 0 || Dv == 0) return ok();
-  return run_dense(q, k, v, mask, mask_kind, mask_vec, is_causal ? 1 : 0, sc, out, lse, Lk,
-                   (hipStream_t)stream);
+  return run_dense(q, k, v, mask, mask_kind, mask_vec, mask_lds, is_causal ? 1 : 0, sc, out, lse,
+                   Lk, (hipStream_t)stream);
 }
 
 size_t wf_varlen_mla_prefill_workspace_size(int batch, int64_t total_q_tokens, int head_num) {
@@ -622,7 +630,7 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   if (n_splits > kMaxSplits) n_splits = kMaxSplits;
   if (n_splits > n_kt) n_splits = n_kt;
   if (n_splits <= 1)
-    return run_dense(q, k_cache, v_cache, nullptr, wf::MASK_NONE, false, 0, sc, out, nullptr,
+    return run_dense(q, k_cache, v_cache, nullptr, wf::MASK_NONE, false, false, 0, sc, out, nullptr,
                      n_vis, (hipStream_t)stream);
   const int tps = (n_kt + n_splits - 1) / n_splits;
   n_splits = (n_kt + tps - 1) / tps;
