@@ -206,7 +206,7 @@ struct AttnFwdP {
     struct Cursor {
       int k, t, n;
       const char* base;
-      int64_t rem;
+      int rows;   // rows of the tensor left from the tile's first row (key Lk - 64t)
     };
     const int64_t kstep = (int64_t)BN * a.k_sm * 2, vstep = (int64_t)BN * a.v_sm * 2;
     auto enter = [&](Cursor& cu, int k, bool is_v) {
@@ -215,7 +215,7 @@ struct AttnFwdP {
       cu.t = 0;
       if (it.n == 0) {   // past the end: empty descriptors from now on
         cu.n = 0x7fffffff;
-        cu.rem = 0;
+        cu.rows = 0;
         cu.base = (const char*)a.k;
         return;
       }
@@ -223,23 +223,28 @@ struct AttnFwdP {
       const int g = it.hq0 / a.G;
       cu.base = is_v ? (const char*)((const T*)a.v + it.b * a.v_sb + g * a.v_sh)
                      : (const char*)((const T*)a.k + it.b * a.k_sb + g * a.k_sh);
-      cu.rem = (int64_t)a.Lk * (is_v ? a.v_sm : a.k_sm) * 2;
+      cu.rows = a.Lk;
     };
     auto advance = [&](Cursor& cu, bool is_v) {
       if (++cu.t >= cu.n) {
         enter(cu, cu.k + 1, is_v);
       } else {
-        const int64_t st = is_v ? vstep : kstep;
-        cu.base += st;
-        cu.rem -= st;
+        cu.base += is_v ? vstep : kstep;
+        cu.rows -= BN;
       }
     };
     Cursor ck, cv;  // the K copy runs two tiles ahead of the compute, the V copy one
-    // Copy i of the tile the cursor points at.
+    // Copy i of the tile the cursor points at: rows [i*ROWS, (i+1)*ROWS) of the tile, with a
+    // descriptor that ends after the rows the tensor still has (32-bit arithmetic: a tile
+    // spans less than 2 GiB).
     auto issue_one = [&](const Cursor& cu, bool is_v, WF_LDS char* dst, int i) {
-      const int64_t off = (int64_t)i * (is_v ? VROWS * vsm2 : KROWS * ksm2);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(cu.base + off, cu.rem - off),
-                                               (WF_LDS void*)(dst + (i * NW + w) * 1024), 16,
+      const int rows_per = is_v ? VROWS : KROWS;
+      const uint32_t sm2 = is_v ? vsm2 : ksm2;
+      int r = cu.rows - i * rows_per;
+      r = r < 0 ? 0 : r > rows_per ? rows_per : r;
+      const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(cu.base + (int64_t)i * rows_per * sm2), 0, (int)((uint32_t)r * sm2), 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (WF_LDS void*)(dst + (i * NW + w) * 1024), 16,
                                                (int)(is_v ? vvo : kvo), 0, 0, 0);
     };
     auto issue = [&](const Cursor& cu, bool is_v, WF_LDS char* dst) {
