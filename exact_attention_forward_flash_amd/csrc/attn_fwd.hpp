@@ -417,10 +417,15 @@ struct AttnFwd {
 
     // Phase A: p = exp2(scale*log2e*s - m) for the current tile (packed to 16 bits as the
     // P^T operand) while, if there is a next tile, its S^T MFMAs are issued in between.
+    // A wave in phase A issues ahead of one in phase B (s_setprio), and the packed weights are
+    // pinned at its end so that the exponentials stay among the S^T MFMAs (not with the
+    // 192-wide MLA score, whose Q^T operands leave no registers for it).
+    constexpr bool PIN = DQK <= 128;
     auto phase_a = [&](const WF_LDS char* Kn, auto has_next_c, f32x16* cur, f32x16* nxt) {
       constexpr bool has_next = decltype(has_next_c)::value;
       const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
       float psum = 0.f;
+      if (PIN) __builtin_amdgcn_s_setprio(3);
       if constexpr (has_next) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -451,7 +456,11 @@ struct AttnFwd {
       }
       l_run += psum;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) pk[m] = pack8<T>(cur[m >> 1], 8 * (m & 1));
+      for (int m = 0; m < 4; ++m) {
+        pk[m] = pack8<T>(cur[m >> 1], 8 * (m & 1));
+        if (PIN) asm volatile("" ::"v"(pk[m]));
+      }
+      if (PIN) __builtin_amdgcn_s_setprio(0);
     };
 
     // Phase B: O^T += V^T P^T for the current tile while, if there is a next tile, its row
