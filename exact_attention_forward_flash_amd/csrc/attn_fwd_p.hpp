@@ -241,7 +241,9 @@ struct AttnFwdP {
       const int rows_per = is_v ? VROWS : KROWS;
       const uint32_t sm2 = is_v ? vsm2 : ksm2;
       int r = cu.rows - i * rows_per;
-      r = r < 0 ? 0 : r > rows_per ? rows_per : r;
+      // The clamp becomes a vector med3; read it back into a scalar register, or the
+      // descriptor lands in vector registers and the load is wrapped in a per-lane loop.
+      r = __builtin_amdgcn_readfirstlane(r < 0 ? 0 : r > rows_per ? rows_per : r);
       const auto rs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(cu.base + (int64_t)i * rows_per * sm2), 0, (int)((uint32_t)r * sm2), 0x00020000);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (WF_LDS void*)(dst + (i * NW + w) * 1024), 16,
