@@ -71,12 +71,19 @@ def varlen_mla_prefill_workspace_size(batch, total_q_tokens, head_num):
 
 
 def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, kv_head_num,
-                       qk_scale, mask_type=1, workspace=None):
-    """Packed varlen MLA prefill: q [nTq,Hq,128], q_rope [nTq,Hq,64], k/v [nTk,Hkv,128],
-    k_rope [nTk,Hkv,64], device int32 lengths [batch]; mask_type 0 = none, 1 = causal
-    (bottom-right). Returns out [nTq, Hq, 128]."""
+                       qk_scale, mask_type=1, workspace=None, kv_layout="packed"):
+    """Varlen MLA prefill: q [nTq,Hq,128], q_rope [nTq,Hq,64], device int32 lengths [batch];
+    mask_type 0 = none, 1 = causal (bottom-right). K/V come packed (kv_layout "packed":
+    k/v [nTk,Hkv,128], k_rope [nTk,Hkv,64]) or padded per sequence (kv_layout "padded":
+    k/v [batch,max_seq,Hkv*128] or [batch,max_seq,Hkv,128], k_rope likewise with 64).
+    Returns out [nTq, Hq, 128]."""
     lib = _lib.load()
     batch = int(q_seqlen.numel())
+    if kv_layout == "padded":
+        k, k_rope, v = (t if t.dim() == 4 else t.view(t.shape[0], t.shape[1], int(kv_head_num), -1)
+                        for t in (k, k_rope, v))
+    elif kv_layout != "packed":
+        raise ValueError("kv_layout must be 'packed' or 'padded'")
     n_q = q.shape[0]
     out = torch.empty((n_q, head_num, v.shape[-1]), dtype=q.dtype, device=q.device)
     need = varlen_mla_prefill_workspace_size(batch, n_q, head_num)

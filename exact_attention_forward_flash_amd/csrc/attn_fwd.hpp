@@ -56,6 +56,7 @@ struct FwdArgs {
   float inv_scale;    // 1 / scale (float masks are added to raw scores as mask / scale)
   // varlen (persistent) mode
   const int* cu_q; const int* cu_k; const int2* items; int* counter; const int* n_items;
+  int kv_padded;      // K/V rows of sequence i start at i * k_sb (padded), not at cu_k[i]
   // split-KV mode
   int tiles_per_split; float* part_o; float* part_lse;
 };
@@ -645,7 +646,7 @@ __device__ __forceinline__ void attn_dispatch(const FwdArgs& a, const RunItem& r
       it.Lq = a.cu_q[it.b + 1] - cq0;
       it.Lk = a.cu_k[it.b + 1] - ck0;
       it.qtok0 = cq0;
-      it.ktok0 = ck0;
+      it.ktok0 = a.kv_padded ? 0 : ck0;
       it.shift = CAUSAL ? it.Lk - it.Lq : 0;
       it.split = -1;
       it.kt_lo = 0;

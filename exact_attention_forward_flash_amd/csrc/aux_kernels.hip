@@ -8,6 +8,8 @@ namespace wf {
 // Varlen tile schedule (packed sequences given by per-sequence lengths, Ascend "MLA Prefill"
 // qSeqLen / kvSeqLen).
 //   cu_q, cu_k = exclusive prefix sums of the lengths ([batch + 1]);
+//   max_kv >= 0: keys and values are padded per sequence (max_kv rows each), so a sequence's
+//   kv length may not exceed max_kv and the packed total is not checked;
 //   one work item per (sequence, query tile of bmp positions), ordered by descending
 //   number of key tiles (longest first, so persistent work groups finish together).
 // One work group of 1024 threads; the attention kernel that follows on the stream takes
@@ -16,17 +18,18 @@ namespace wf {
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBuckets = 2048;
 
-__device__ int block_exclusive_scan(int v, int* sm, int* total) {
+template <typename I>
+__device__ I block_exclusive_scan(I v, I* sm, I* total) {
   const int t = threadIdx.x;
   sm[t] = v;
   __syncthreads();
   for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int x = t >= off ? sm[t - off] : 0;
+    const I x = t >= off ? sm[t - off] : 0;
     __syncthreads();
     sm[t] += x;
     __syncthreads();
   }
-  const int incl = sm[t];
+  const I incl = sm[t];
   *total = sm[kSchedThreads - 1];
   __syncthreads();
   return incl - v;
@@ -34,8 +37,9 @@ __device__ int block_exclusive_scan(int v, int* sm, int* total) {
 
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch, int64_t total_q,
-    int64_t total_k, int bmp, int bn, int causal, int max_items, int* ws) {
+    int64_t total_k, int max_kv, int bmp, int bn, int causal, int max_items, int* ws) {
   __shared__ int sm[kSchedThreads];
+  __shared__ int64_t sm64[kSchedThreads];  // length sums: 1024 int32 lengths can overflow 32 bits
   __shared__ int hist[kSchedBuckets];
   __shared__ int s_bad;
   int* cu_q = (int*)((char*)ws + VarlenWs::cu_q_off());
@@ -49,22 +53,24 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
   // Prefix sums over the batch, 1024 sequences at a time. Totals are kept in 64 bits to
   // reject lengths that overflow.
   int64_t carry_q = 0, carry_k = 0;
-  int carry_items = 0;
+  int64_t carry_items = 0;
   for (int base = 0; base < batch; base += kSchedThreads) {
     const int bi = base + t;
     int lq = 0, lk = 0;
     if (bi < batch) {
       lq = q_seqlen[bi];
       lk = kv_seqlen[bi];
-      if (lq < 0 || lk < 0) s_bad = 1;
+      if (lq < 0 || lk < 0 || (max_kv >= 0 && lk > max_kv)) s_bad = 1;
     }
     lq = lq < 0 ? 0 : lq;
     lk = lk < 0 ? 0 : lk;
-    int tot_q, tot_k, tot_i;
-    const int eq = block_exclusive_scan(lq, sm, &tot_q);
-    const int ek = block_exclusive_scan(lk, sm, &tot_k);
-    const int ntile = (lq + bmp - 1) / bmp;
-    block_exclusive_scan(ntile, sm, &tot_i);
+    int64_t tot_q, tot_k;
+    int64_t tot_i;
+    const int64_t eq = block_exclusive_scan<int64_t>(lq, sm64, &tot_q);
+    const int64_t ek = block_exclusive_scan<int64_t>(lk, sm64, &tot_k);
+    const int64_t ntile = ((int64_t)lq + bmp - 1) / bmp;
+    block_exclusive_scan<int64_t>(ntile, sm64, &tot_i);
+    // Offsets past 2^31 are never used: the totals below flag the call as bad.
     if (bi < batch) {
       cu_q[bi] = (int)(carry_q + eq);
       cu_k[bi] = (int)(carry_k + ek);
@@ -77,11 +83,13 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
   if (t == 0) {
     cu_q[batch] = (int)carry_q;
     cu_k[batch] = (int)carry_k;
-    if (carry_q > total_q || carry_k > total_k || carry_items > max_items) s_bad = 1;
+    if (carry_q > total_q || (max_kv < 0 && carry_k > total_k) || carry_k > 0x7fffffff ||
+        carry_items > max_items)
+      s_bad = 1;
   }
   __syncthreads();
   const int bad = s_bad;
-  const int n_pairs = bad ? 0 : carry_items;
+  const int n_pairs = bad ? 0 : (int)carry_items;
 
   // Counting sort of the (sequence, query tile) items by descending key-tile count. Pass 0
   // builds the histogram, then its exclusive scan turns counts into slot offsets; pass 1
@@ -93,13 +101,13 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
         if (bi < batch) {
           const int lq = cu_q[bi + 1] - cu_q[bi];
           const int lk = cu_k[bi + 1] - cu_k[bi];
-          const int ntile = (lq + bmp - 1) / bmp;
-          const int n_kt = (lk + bn - 1) / bn;
+          const int ntile = (int)(((int64_t)lq + bmp - 1) / bmp);
+          const int n_kt = (int)(((int64_t)lk + bn - 1) / bn);
           for (int tt = 0; tt < ntile; ++tt) {
             int cost = n_kt;
             if (causal) {
-              const int lim = tt * bmp + bmp - 1 + (lk - lq);
-              cost = lim < 0 ? 0 : (lim / bn + 1 < n_kt ? lim / bn + 1 : n_kt);
+              const int64_t lim = (int64_t)tt * bmp + bmp - 1 + ((int64_t)lk - lq);
+              cost = lim < 0 ? 0 : (lim / bn + 1 < n_kt ? (int)(lim / bn + 1) : n_kt);
             }
             const int bucket =
                 kSchedBuckets - 1 - (cost < kSchedBuckets - 1 ? cost : kSchedBuckets - 1);
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
         int run = 0;
         for (int base = 0; base < kSchedBuckets; base += kSchedThreads) {
           int tot;
-          const int ex = block_exclusive_scan(hist[base + t], sm, &tot);
+          const int ex = block_exclusive_scan<int>(hist[base + t], sm, &tot);
           hist[base + t] = run + ex;
           run += tot;
           __syncthreads();
@@ -133,10 +141,10 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
 }
 
 hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
-                                  int64_t total_q, int64_t total_k, int bmp, int bn, int causal,
-                                  int max_items, int* ws, hipStream_t s) {
+                                  int64_t total_q, int64_t total_k, int max_kv, int bmp, int bn,
+                                  int causal, int max_items, int* ws, hipStream_t s) {
   hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, q_seqlen,
-                     kv_seqlen, batch, total_q, total_k, bmp, bn, causal, max_items, ws);
+                     kv_seqlen, batch, total_q, total_k, max_kv, bmp, bn, causal, max_items, ws);
   return hipGetLastError();
 }
 

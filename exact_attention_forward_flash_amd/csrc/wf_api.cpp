@@ -407,6 +407,27 @@ static int as3d(const wf_tensor* t, const char* name, int64_t heads, wf_tensor* 
   return check_data(o, name, 3);
 }
 
+// K, kRope and V are packed ([nTk, Hkv, d] or flat) or padded per sequence
+// ([batch, max_seq, Hkv, d]: sequence i's keys are rows [0, kv_seqlen[i]) of entry i). The
+// padded form comes back as a [max_seq, Hkv, d] view plus its batch stride (0 when packed).
+static int kv_view(const wf_tensor* t, const char* name, int64_t heads, int batch, wf_tensor* o,
+                   int64_t* sb) {
+  *sb = 0;
+  if (t == nullptr || t->ndim != 4) return as3d(t, name, heads, o);
+  int rc = check_data(t, name, 4);
+  if (rc) return rc;
+  if (t->shape[0] != batch)
+    return fail(WF_ERR_SHAPE, "%s: the padded form is [batch=%d, max_seq, H, d]", name, batch);
+  *o = *t;
+  o->ndim = 3;
+  for (int i = 0; i < 3; ++i) {
+    o->shape[i] = t->shape[i + 1];
+    o->stride[i] = t->stride[i + 1];
+  }
+  *sb = t->stride[0];
+  return check_data(o, name, 3);
+}
+
 int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const wf_tensor* k_,
                           const wf_tensor* k_rope_, const wf_tensor* v_,
                           const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
@@ -415,10 +436,15 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
                           void* stream) {
   int rc;
   wf_tensor q, qr, k, kr, v, out;
+  int64_t k_sb, kr_sb, v_sb;
   if ((rc = as3d(q_, "q", head_num, &q)) || (rc = as3d(q_rope_, "q_rope", head_num, &qr)) ||
-      (rc = as3d(k_, "k", kv_head_num, &k)) || (rc = as3d(k_rope_, "k_rope", kv_head_num, &kr)) ||
-      (rc = as3d(v_, "v", kv_head_num, &v)) || (rc = as3d(out_, "out", head_num, &out)))
+      (rc = kv_view(k_, "k", kv_head_num, batch, &k, &k_sb)) ||
+      (rc = kv_view(k_rope_, "k_rope", kv_head_num, batch, &kr, &kr_sb)) ||
+      (rc = kv_view(v_, "v", kv_head_num, batch, &v, &v_sb)) || (rc = as3d(out_, "out", head_num, &out)))
     return rc;
+  const bool padded = k_->ndim == 4;
+  if ((k_rope_->ndim == 4) != padded || (v_->ndim == 4) != padded)
+    return fail(WF_ERR_LAYOUT, "k, k_rope and v must all be packed or all padded");
   if (q.dtype == WF_F32) return fail(WF_ERR_DTYPE, "MLA prefill takes f16 or bf16");
   if (qr.dtype != q.dtype || k.dtype != q.dtype || kr.dtype != q.dtype || v.dtype != q.dtype ||
       out.dtype != q.dtype)
@@ -439,7 +465,8 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
   if (mask_type != 0 && mask_type != 1)
     return fail(WF_ERR_UNSUPPORTED, "mask_type must be 0 (none) or 1 (causal)");
   if (batch < 0) return fail(WF_ERR_SHAPE, "batch must be >= 0");
-  if (nTq > 0x7fffffff || nTk > 0x7fffffff) return fail(WF_ERR_SHAPE, "token count exceeds 2^31");
+  if (nTq > 0x7fffffff || nTk > 0x7fffffff || (padded && (int64_t)batch * nTk > 0x7fffffff))
+    return fail(WF_ERR_SHAPE, "token count exceeds 2^31");
   float sc;
   if ((rc = resolve_scale(qk_scale, Dv + 64, &sc))) return rc;
   if (batch > 0 && (q_seqlen == nullptr || kv_seqlen == nullptr))
@@ -457,17 +484,19 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
   const int max_items = (int)(nTq / e->bmp + batch);
   int* ws = (int*)workspace;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t he = wf::launch_varlen_schedule(q_seqlen, kv_seqlen, batch, nTq, nTk, e->bmp, e->bn,
-                                             mask_type, max_items, ws, s);
+  hipError_t he = wf::launch_varlen_schedule(q_seqlen, kv_seqlen, batch, nTq, nTk,
+                                             padded ? (int)nTk : -1, e->bmp, e->bn, mask_type,
+                                             max_items, ws, s);
   if (he != hipSuccess) return hip_status(he, "schedule launch");
   wf::FwdArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = q.data; a.q2 = qr.data; a.k = k.data; a.k2 = kr.data; a.v = v.data; a.o = out.data;
   a.q_sm = q.stride[0]; a.q_sh = q.stride[1];
   a.q2_sm = qr.stride[0]; a.q2_sh = qr.stride[1];
-  a.k_sm = k.stride[0]; a.k_sh = k.stride[1];
-  a.k2_sm = kr.stride[0]; a.k2_sh = kr.stride[1];
-  a.v_sm = v.stride[0]; a.v_sh = v.stride[1];
+  a.k_sm = k.stride[0]; a.k_sh = k.stride[1]; a.k_sb = k_sb;
+  a.k2_sm = kr.stride[0]; a.k2_sh = kr.stride[1]; a.k2_sb = kr_sb;
+  a.v_sm = v.stride[0]; a.v_sh = v.stride[1]; a.v_sb = v_sb;
+  a.kv_padded = padded ? 1 : 0;
   a.o_sm = out.stride[0]; a.o_sh = out.stride[1];
   a.B = batch; a.Hq = head_num; a.Hkv = kv_head_num; a.G = head_num / kv_head_num;
   a.scale_log2 = sc * wf::kLog2e;

@@ -66,8 +66,8 @@ const F32Entry* attn_table_f32(int* n);
 
 // Auxiliary kernels.
 hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
-                                  int64_t total_q, int64_t total_k, int bmp, int bn, int causal,
-                                  int max_items, int* ws, hipStream_t s);
+                                  int64_t total_q, int64_t total_k, int max_kv, int bmp, int bn,
+                                  int causal, int max_items, int* ws, hipStream_t s);
 hipError_t launch_split_combine(int dtype, const float* part_o, const float* part_lse,
                                 int n_splits, int B, int Hq, int Lq, int Dv, void* out,
                                 int64_t o_sb, int64_t o_sh, int64_t o_sm, hipStream_t s);

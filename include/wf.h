@@ -100,11 +100,15 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
  *
  *   q       [nTq, Hq,  Dv]  f16 | bf16 (the value-width "nope" part of the query)
  *   q_rope  [nTq, Hq,  64]  rotary part of the query (same dtype)
- *   k       [nTk, Hkv, Dv]  k_rope [nTk, Hkv, 64]   v [nTk, Hkv, Dv]
+ *   k       [nTk, Hkv, Dv]  k_rope [nTk, Hkv, 64]   v [nTk, Hkv, Dv]   (packed), or
+ *           [batch, max_seq, Hkv, Dv] / [batch, max_seq, Hkv, 64] / [batch, max_seq, Hkv, Dv]
+ *           (padded: the page's [batch, max_seq, kv_head*d] viewed with the head split
+ *           out). All three take the same form; a 4-d k means padded.
  *           A concatenated cache (k_rope stored right after k in each token row) is the
- *           same call with k_rope->data = k->data + Dv and matching strides.
+ *           same call with k_rope->data = k->data + Dv and matching strides, in either form.
  *   q_seqlen, kv_seqlen  device int32 [batch]; sequence i owns query tokens
- *           [sum_{t<i} q_seqlen[t], ... + q_seqlen[i]) and likewise for keys/values.
+ *           [sum_{t<i} q_seqlen[t], ... + q_seqlen[i]) and likewise for packed keys/values;
+ *           with padded keys/values it owns rows [0, kv_seqlen[i]) of batch entry i.
  *   head_num, kv_head_num  Hq, Hkv (Hq a multiple of Hkv; q head h reads kv head
  *           h / (Hq/Hkv)).
  *   qk_scale  multiplies (q . k + q_rope . k_rope); finite and > 0.
@@ -115,8 +119,9 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
  *           wf_varlen_mla_prefill_workspace_size(batch, nTq, head_num) bytes, 256-byte
  *           aligned; it holds the tile schedule built on the device from the lengths.
  * Score width is Dv + 64 with Dv = 128 (the built instantiation).
- * If the device lengths are negative or sum past nTq / nTk, no attention is computed and
- * word 2 of the workspace (int32) is set to 1; it is 0 after a good call.
+ * If the device lengths are negative, sum past nTq (or, packed, nTk) or, padded, exceed
+ * max_seq, no attention is computed and word 2 of the workspace (int32) is set to 1; it is 0
+ * after a good call. A mix of packed and padded k / k_rope / v is WF_ERR_LAYOUT.
  * ------------------------------------------------------------------------------------- */
 size_t wf_varlen_mla_prefill_workspace_size(int batch, int64_t total_q_tokens, int head_num);
 int wf_varlen_mla_prefill(const wf_tensor* q, const wf_tensor* q_rope, const wf_tensor* k,

@@ -29,7 +29,8 @@ Parity pins (tests/test_oracle.py): torch's CPU fp64 scaled_dot_product_attentio
 (library routine), closed forms (single key -> that V row; zero keys -> mean of V),
 invariants (kept-all bool mask = no mask, bool = float where(M,0,-inf), causal = float
 triangle, per-row constant shift, scale folding, key permutation, GQA = repeated heads),
-MLA = SDPA on concatenated [q|qRope],[k|kRope] per sequence, packing invariance.
+MLA = SDPA on concatenated [q|qRope],[k|kRope] per sequence, packing invariance,
+padded K/V = the same rows packed.
 """
 from __future__ import annotations
 
@@ -131,11 +132,17 @@ def cu_seqlens(lengths):
 
 
 def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num,
-                       kv_head_num, qk_scale, mask_type=MASK_NONE, row_block=512):
+                       kv_head_num, qk_scale, mask_type=MASK_NONE, row_block=512,
+                       kv_layout="packed"):
     """MLA prefill over a packed batch (Ascend "MLA Prefill" parameter table).
 
     q [nTq, Hq*Dv] or [nTq, Hq, Dv]; q_rope [nTq, Hq*64] or [nTq, Hq, 64];
-    k, v [nTk, Hkv, Dv]; k_rope [nTk, Hkv, 64]; q_seqlen, kv_seqlen int [batch].
+    q_seqlen, kv_seqlen int [batch]. The table gives K, kRope and V in two forms:
+      kv_layout "packed": k, v [nTk, Hkv*Dv] or [nTk, Hkv, Dv], k_rope [nTk, Hkv*64] or
+        [nTk, Hkv, 64]; sequence i owns the kv_seqlen[i] rows after those of sequences < i;
+      kv_layout "padded": k, v [batch, max_seq, Hkv*Dv] or [batch, max_seq, Hkv, Dv],
+        k_rope [batch, max_seq, Hkv*64] or [..., Hkv, 64]; sequence i owns rows
+        [0, kv_seqlen[i]) of batch entry i.
     For sequence i the score is qk_scale * (q . k + qRope . kRope) over that sequence's
     own tokens only; mask_type 1 applies bottom-right causal masking.
     Returns out [nTq, Hq, Dv] as float64.
@@ -149,28 +156,49 @@ def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num,
     q = _f64(q)
     q = q.reshape(q.shape[0], Hq, -1)
     qr = _f64(q_rope).reshape(q.shape[0], Hq, -1)
-    k = _f64(k)
-    k = k.reshape(k.shape[0], Hkv, -1)
-    kr = _f64(k_rope).reshape(k.shape[0], Hkv, -1)
-    v = _f64(v)
-    v = v.reshape(v.shape[0], Hkv, -1)
     cq, ck = cu_seqlens(q_seqlen), cu_seqlens(kv_seqlen)
     if len(cq) != len(ck):
         raise ValueError("qSeqLen and kvSeqLen lengths differ")
-    if cq[-1] > q.shape[0] or ck[-1] > k.shape[0]:
+    if kv_layout == "packed":
+        k = _f64(k)
+        k = k.reshape(k.shape[0], Hkv, -1)
+        kr = _f64(k_rope).reshape(k.shape[0], Hkv, -1)
+        v = _f64(v)
+        v = v.reshape(v.shape[0], Hkv, -1)
+        if ck[-1] > k.shape[0]:
+            raise ValueError("sequence lengths exceed the packed token count")
+
+        def kv_rows(i):  # sequence i's keys, rotary keys and values [lk, Hkv, d]
+            return k[ck[i]:ck[i + 1]], kr[ck[i]:ck[i + 1]], v[ck[i]:ck[i + 1]]
+    elif kv_layout == "padded":
+        k = _f64(k)
+        k = k.reshape(k.shape[0], k.shape[1], Hkv, -1)
+        kr = _f64(k_rope).reshape(k.shape[0], k.shape[1], Hkv, -1)
+        v = _f64(v)
+        v = v.reshape(v.shape[0], v.shape[1], Hkv, -1)
+        if k.shape[0] != len(ck) - 1:
+            raise ValueError("padded K/V need one batch entry per sequence")
+        if len(ck) > 1 and np.diff(ck).max() > k.shape[1]:
+            raise ValueError("a kv length exceeds max_seq")
+
+        def kv_rows(i):
+            lk_i = ck[i + 1] - ck[i]
+            return k[i, :lk_i], kr[i, :lk_i], v[i, :lk_i]
+    else:
+        raise ValueError("kv_layout must be 'packed' or 'padded'")
+    if cq[-1] > q.shape[0]:
         raise ValueError("sequence lengths exceed the packed token count")
     scale = float(qk_scale)
-    out = np.zeros((q.shape[0], Hq, v.shape[2]), dtype=np.float64)
+    out = np.zeros((q.shape[0], Hq, v.shape[-1]), dtype=np.float64)
     for i in range(len(cq) - 1):
         lq, lk = cq[i + 1] - cq[i], ck[i + 1] - ck[i]
         if lq == 0:
             continue
         jj = np.arange(lk)
+        ki, kri, vi = kv_rows(i)
         for h in range(Hq):
             g = h // G
-            kg = k[ck[i]:ck[i + 1], g]
-            krg = kr[ck[i]:ck[i + 1], g]
-            vg = v[ck[i]:ck[i + 1], g]
+            kg, krg, vg = ki[:, g], kri[:, g], vi[:, g]
             for r0 in range(0, lq, row_block):
                 r1 = min(lq, r0 + row_block)
                 rows = slice(cq[i] + r0, cq[i] + r1)

@@ -119,6 +119,13 @@ def test_mla_validation_errors(lib):
     assert call(scale=0.0) == UNSUP
     # the flat [nTokens, H*d] form is accepted (and empty batch launches nothing)
     assert call(q=T([n, H * 128]), out=T([n, H * 128]), batch=0) == OK
+    # padded K/V [batch, max_seq, Hkv, d]: all three padded, one batch entry per sequence
+    pk, pkr, pv = T([3, 40, H, 128]), T([3, 40, H, 64]), T([3, 40, H, 128])
+    assert call(k=pk, kr=pkr, v=pv, batch=3, ws=None) == WS      # layout accepted up to the workspace
+    assert call(k=pk, kr=kr, v=pv) == LAYOUT                      # mixed packed / padded
+    assert call(k=pk, kr=pkr, v=T([3, 40, H, 64])) == SHAPE       # value width
+    assert call(k=T([2, 40, H, 128]), kr=T([2, 40, H, 64]), v=T([2, 40, H, 128])) == SHAPE  # batch
+    assert call(k=T([0, 40, H, 128]), kr=T([0, 40, H, 64]), v=T([0, 40, H, 128]), batch=0) == OK
 
 
 def _state(lib, L, sink, window, chunk):

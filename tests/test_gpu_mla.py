@@ -66,6 +66,62 @@ def test_flat_layout_and_concatenated_cache():
     assert torch.equal(out, ref)
 
 
+def _padded(w, max_seq, fill=float("nan")):
+    """The packed K/V of w laid out padded per sequence [batch, max_seq, Hkv, d]; rows past a
+    sequence's kv length hold `fill` (NaN: any read of them would reach the output)."""
+    kvl = w["kv_seqlen"].tolist()
+    cu = np.concatenate([[0], np.cumsum(kvl)])
+    out = {}
+    for n in ("k", "k_rope", "v"):
+        t = w[n]
+        pad = torch.full((len(kvl), max_seq) + tuple(t.shape[1:]), fill, dtype=t.dtype)
+        for i, lk in enumerate(kvl):
+            pad[i, :lk] = t[cu[i]:cu[i + 1]]
+        out[n] = pad
+    return out
+
+
+PADDED = [  # q lengths, kv lengths, max_seq, H, Hkv, dtype, mask_type
+    ([1, 63, 300, 0, 777], [1, 63, 300, 0, 777], 800, 4, 4, "bf16", 1),
+    ([200, 31, 513], [260, 31, 600], 640, 4, 2, "bf16", 1),
+    ([257, 100], [257, 90], 257, 2, 1, "fp16", 0),
+]
+
+
+@pytest.mark.parametrize("case", PADDED, ids=[str(c) for c in PADDED])
+def test_padded_kv_layout(case):
+    # [MLA] table: K/kRope/V may also come as [batch, max_seq, kv_head*d].
+    qlens, kvlens, max_seq, H, Hkv, dt, mt = case
+    w = _inputs(qlens, kvlens, H, Hkv, dt, seed=7, mask_type=mt)
+    p = _padded(w, max_seq)
+    t = {n: w[n].to(DEV) for n in ("q", "q_rope", "q_seqlen", "kv_seqlen")}
+    pd = {n: p[n].to(DEV) for n in p}
+    flat = {n: pd[n].reshape(len(kvlens), max_seq, -1) for n in pd}   # the page's 3-d form
+    out = varlen_mla_prefill(t["q"], t["q_rope"], flat["k"], flat["k_rope"], flat["v"],
+                             t["q_seqlen"], t["kv_seqlen"], H, Hkv, w["qk_scale"], mt,
+                             kv_layout="padded")
+    ref = oracle.varlen_mla_prefill(w["q"], w["q_rope"], p["k"], p["k_rope"], p["v"],
+                                    w["q_seqlen"], w["kv_seqlen"], H, Hkv,
+                                    np.float32(w["qk_scale"]), mt, kv_layout="padded")
+    assert_close(out, ref, w["q"].dtype, str(case))
+    # the same tokens packed give the same bits (same kernel, same order)
+    assert torch.equal(out, _gpu(w))
+
+
+def test_padded_kv_longer_than_max_seq_sets_the_error_word():
+    w = _inputs([64, 64], [64, 64], 2, 2, "bf16", seed=8)
+    p = _padded(w, 64, fill=0.0)
+    t = {n: w[n].to(DEV) for n in ("q", "q_rope")}
+    pd = {n: p[n].to(DEV) for n in p}
+    long_kv = torch.tensor([64, 65], dtype=torch.int32, device=DEV)
+    ql = torch.tensor([64, 64], dtype=torch.int32, device=DEV)
+    ws = torch.zeros(varlen_mla_prefill_workspace_size(2, 128, 2), dtype=torch.uint8, device=DEV)
+    varlen_mla_prefill(t["q"], t["q_rope"], pd["k"], pd["k_rope"], pd["v"], ql, long_kv, 2, 2,
+                       w["qk_scale"], 1, workspace=ws, kv_layout="padded")
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[2]) == 1
+
+
 def test_bad_lengths_set_the_error_word_and_compute_nothing():
     w = _inputs([100, 300], [100, 300], 2, 2, "bf16", seed=5)
     t = {n: w[n].to(DEV) for n in ("q", "q_rope", "k", "k_rope", "v")}

@@ -211,6 +211,47 @@ def test_mla_equals_sdpa_on_concatenated_dims(mask_type):
         np.testing.assert_allclose(out[a:b], ref.transpose(1, 0, 2), **TIGHT)
 
 
+@pytest.mark.parametrize("mask_type", [0, 1])
+def test_mla_padded_kv_equals_sdpa_per_sequence(mask_type):
+    # The table's padded form [batch, max_seq, kv_head*d]: sequence i reads rows
+    # [0, kv_len[i]) of entry i; the padding rows (filled with large values here) are unused.
+    qlens, kvlens, max_seq = [5, 1, 7], [6, 3, 7], 9
+    H, Hkv, scale, dv, dr = 4, 2, 0.21, 16, 8
+    q, qr, _, _, _ = _mla_inputs(qlens, kvlens, H, Hkv, dv, dr)
+    kp = _t((3, max_seq, Hkv, dv), 90) + 0.0
+    krp = _t((3, max_seq, Hkv, dr), 91) + 0.0
+    vp = _t((3, max_seq, Hkv, dv), 92) + 0.0
+    for i, lk in enumerate(kvlens):
+        kp[i, lk:] = 50.0
+        krp[i, lk:] = -40.0
+        vp[i, lk:] = 1e3
+    out = varlen_mla_prefill(q, qr, kp.reshape(3, max_seq, -1), krp, vp, qlens, kvlens, H, Hkv,
+                             scale, mask_type, kv_layout="padded")
+    cq = cu_seqlens(qlens)
+    G = H // Hkv
+    for i, (lq, lk) in enumerate(zip(qlens, kvlens)):
+        a, b = cq[i], cq[i + 1]
+        qc = torch.cat([q[a:b], qr[a:b]], dim=-1).permute(1, 0, 2)[None]
+        kc = torch.cat([kp[i, :lk], krp[i, :lk]], dim=-1).permute(1, 0, 2)[None]
+        vc = vp[i, :lk].permute(1, 0, 2)[None]
+        kc = kc.repeat_interleave(G, dim=1)
+        vc = vc.repeat_interleave(G, dim=1)
+        if mask_type:  # bottom-right: query r keeps key j <= r + lk - lq
+            keep = torch.arange(lk)[None, :] <= torch.arange(lq)[:, None] + (lk - lq)
+            ref = _torch_sdpa(qc, kc, vc, scale=scale, attn_mask=keep)[0]
+        else:
+            ref = _torch_sdpa(qc, kc, vc, scale=scale)[0]
+        np.testing.assert_allclose(out[a:b], ref.transpose(1, 0, 2), **TIGHT)
+
+
+def test_mla_padded_kv_rejects_long_sequence():
+    q, qr, _, _, _ = _mla_inputs([2], [2], 2, 2)
+    kp, vp = _t((1, 3, 2, 16), 1), _t((1, 3, 2, 16), 2)
+    with pytest.raises(ValueError):
+        varlen_mla_prefill(q, qr, kp, _t((1, 3, 2, 8), 3), vp, [2], [4], 2, 2, 0.3, 0,
+                           kv_layout="padded")
+
+
 def test_mla_flat_layout_equals_3d_layout():
     lengths = [3, 9]
     q, qr, k, kr, v = _mla_inputs(lengths, lengths, 2, 2)

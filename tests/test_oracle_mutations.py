@@ -25,8 +25,10 @@ MUTATIONS = [
     ("attention", "keep &= bmask[b, h, r0:r1]", "keep &= ~bmask[b, h, r0:r1]", "bool mask polarity"),
     ("attention", "+ qr[rows, h] @ krg.T", "", "rope term dropped"),
     ("attention", "ii + (lk - lq)", "ii", "MLA bottom-right offset"),
-    ("attention", "vg = v[ck[i]:ck[i + 1], g]", "vg = v[cq[i]:cq[i + 1], g]", "value range of the wrong sequence side"),
-    ("attention", "kg = k[ck[i]:ck[i + 1], g]", "kg = k[ck[i]:ck[i + 1], 0]", "MLA kv head fixed"),
+    ("attention", "v[ck[i]:ck[i + 1]]\n", "v[cq[i]:cq[i + 1]]\n", "value range of the wrong sequence side"),
+    ("attention", "kg, krg, vg = ki[:, g], kri[:, g], vi[:, g]", "kg, krg, vg = ki[:, 0], kri[:, g], vi[:, g]", "MLA kv head fixed"),
+    ("attention", "return k[i, :lk_i], kr[i, :lk_i], v[i, :lk_i]", "return k[0, :lk_i], kr[i, :lk_i], v[i, :lk_i]", "padded K of the wrong batch entry"),
+    ("attention", "return k[i, :lk_i], kr[i, :lk_i], v[i, :lk_i]", "return k[i, :lk_i], kr[i, :lk_i], v[i, 1:lk_i + 1]", "padded V rows shifted"),
     ("block_kv_cache", "max(self.sink, T - self.window)", "max(0, T - self.window)", "window start ignores sink"),
     ("block_kv_cache", "(self.last_chunk, self.last_chunk + 1)", "(self.last_chunk, self.last_chunk + 1, self.last_chunk + 2)", "skip allowed"),
     ("block_kv_cache", "min(T, self.sink)", "min(T, self.sink + 1)", "sink length"),
