@@ -205,6 +205,21 @@ def other_workload(name, steps, warmup):
                     update_gbs=round(upd_bytes * reps / (tot_u * 1e-3) / 1e9, 1),
                     attend_ms_per_chunk=round(tot_a / reps / n, 4),
                     attend_tflops=round(fl / (tot_a * 1e-3) / 1e12, 2))
+    elif name == "decode":
+        B, Hq, Hkv, Lk, D = 8, 32, 8, 16384, 128
+        w = synth.random_sdpa_inputs(B, Hq, Hkv, 1, Lk, D, D, "bf16", seed=7)
+        q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
+        ws = torch.empty(max(256, wf.sdpa_decode_workspace_size(q, k, v)), dtype=torch.uint8,
+                         device=dev)
+        out = torch.empty_like(q)
+        ms = _time_steps(lambda: wf.sdpa_decode(q, k, v, scale=w["scale"], workspace=ws),
+                         steps, warmup, stream)
+        ms_dense = _time_steps(lambda: wf.sdpa(q, k, v, scale=w["scale"]), steps, warmup, stream)
+        nbytes = (k.numel() + v.numel() + q.numel() + out.numel()) * 2  # read once + written
+        line.update(ms=round(ms, 4), gbs=round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    hbm_frac=round(nbytes / (ms * 1e-3) / 8e12, 4),
+                    sdpa_fwd_ms=round(ms_dense, 4),
+                    sdpa_fwd_gbs=round(nbytes / (ms_dense * 1e-3) / 1e9, 1))
     else:
         raise SystemExit(f"unknown workload {name}")
     print(json.dumps(line), flush=True)
@@ -220,7 +235,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="causal_gqa",
                     choices=["causal_gqa", "varlen_mla", "masked_bool", "masked_float",
-                             "cache_stream", "page_example"],
+                             "cache_stream", "page_example", "decode"],
                     help="causal_gqa (default) prints the headline line; the others time one of "
                          "the other configurations and print its kernel throughput")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",

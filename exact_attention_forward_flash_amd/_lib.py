@@ -34,6 +34,9 @@ _vp, _i32, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes
 # name -> (restype, argtypes); the full exported surface of include/wf.h
 SIGNATURES = {
     "wf_sdpa_fwd": (_i32, [_T, _T, _T, _T, _i32, _f, _f, _T, ctypes.POINTER(ctypes.c_float), _vp]),
+    "wf_sdpa_decode_workspace_size": (_sz, [_T, _T, _T, _i32]),
+    "wf_sdpa_decode": (_i32, [_T, _T, _T, _i32, _f, _T, ctypes.POINTER(ctypes.c_float), _vp, _sz,
+                              _vp]),
     "wf_varlen_mla_prefill_workspace_size": (_sz, [_i32, _i64, _i32]),
     "wf_varlen_mla_prefill": (_i32, [_T, _T, _T, _T, _T, _vp, _vp, _i32, _i32, _i32, _f, _i32,
                                      _T, _vp, _sz, _vp]),

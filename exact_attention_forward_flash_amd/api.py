@@ -65,6 +65,29 @@ def sdpa(q, k, v, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
     return (out, lse) if return_lse else out
 
 
+def sdpa_decode_workspace_size(q, k, v, is_causal=False):
+    return int(_lib.load().wf_sdpa_decode_workspace_size(_ref(describe(q)), _ref(describe(k)),
+                                                         _ref(describe(v)), int(bool(is_causal))))
+
+
+def sdpa_decode(q, k, v, is_causal=False, scale=None, return_lse=False, workspace=None):
+    """Attention of few queries over a long K/V, split over the keys (decode; speculative
+    decoding when Lq > 1): q [B,Hq,Lq,D], k/v [B,Hkv,Lk,D], D in {64, 128}, 16-bit. is_causal
+    puts the queries at the end of the key sequence (bottom-right). No mask."""
+    lib = _lib.load()
+    out = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    need = sdpa_decode_workspace_size(q, k, v, is_causal)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv, do = describe(q), describe(k), describe(v), describe(out)
+    lse_ptr = ctypes.cast(lse.data_ptr(), ctypes.POINTER(ctypes.c_float)) if lse is not None and lse.numel() else None
+    check(lib.wf_sdpa_decode(_ref(dq), _ref(dk), _ref(dv), int(bool(is_causal)), _scale(scale),
+                             _ref(do), lse_ptr, ctypes.c_void_p(workspace.data_ptr()),
+                             workspace.numel(), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
 def varlen_mla_prefill_workspace_size(batch, total_q_tokens, head_num):
     return int(_lib.load().wf_varlen_mla_prefill_workspace_size(int(batch), int(total_q_tokens),
                                                                 int(head_num)))

@@ -156,7 +156,8 @@ hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seq
 template <typename T>
 __global__ __launch_bounds__(256) void split_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int n_splits,
-    int B, int Hq, int Lq, int Dv, T* out, int64_t o_sb, int64_t o_sh, int64_t o_sm) {
+    int B, int Hq, int Lq, int Dv, T* out, int64_t o_sb, int64_t o_sh, int64_t o_sm,
+    float* lse) {
   const int64_t rows = (int64_t)B * Hq * Lq;
   const int d4 = Dv / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -178,6 +179,8 @@ __global__ __launch_bounds__(256) void split_combine_kernel(
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
+  // lse of the whole row: the splits' lse merged the same way (-inf when no key is kept)
+  if (lse != nullptr && d == 0) lse[row] = den > 0.f ? mx + __logf(den) : -INFINITY;
   const int q = (int)(row % Lq);
   const int hq = (int)((row / Lq) % Hq);
   const int b = (int)(row / ((int64_t)Lq * Hq));
@@ -188,18 +191,19 @@ __global__ __launch_bounds__(256) void split_combine_kernel(
 
 hipError_t launch_split_combine(int dtype, const float* part_o, const float* part_lse,
                                 int n_splits, int B, int Hq, int Lq, int Dv, void* out,
-                                int64_t o_sb, int64_t o_sh, int64_t o_sm, hipStream_t s) {
+                                int64_t o_sb, int64_t o_sh, int64_t o_sm, float* lse,
+                                hipStream_t s) {
   const int64_t n = (int64_t)B * Hq * Lq * (Dv / 4);
   const int blocks = (int)((n + 255) / 256);
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(split_combine_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, part_o,
-                       part_lse, n_splits, B, Hq, Lq, Dv, (__bf16*)out, o_sb, o_sh, o_sm);
+                       part_lse, n_splits, B, Hq, Lq, Dv, (__bf16*)out, o_sb, o_sh, o_sm, lse);
   else if (dtype == DT_F16)
     hipLaunchKernelGGL(split_combine_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, part_o,
-                       part_lse, n_splits, B, Hq, Lq, Dv, (_Float16*)out, o_sb, o_sh, o_sm);
+                       part_lse, n_splits, B, Hq, Lq, Dv, (_Float16*)out, o_sb, o_sh, o_sm, lse);
   else
     hipLaunchKernelGGL(split_combine_kernel<float>, dim3(blocks), dim3(256), 0, s, part_o,
-                       part_lse, n_splits, B, Hq, Lq, Dv, (float*)out, o_sb, o_sh, o_sm);
+                       part_lse, n_splits, B, Hq, Lq, Dv, (float*)out, o_sb, o_sh, o_sm, lse);
   return hipGetLastError();
 }
 

@@ -112,7 +112,8 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
   typedef const wf::AttnEntry* (*TableFn)(int*);
   static const TableFn tables[] = {wf::attn_table_sdpa_bf16_d64, wf::attn_table_sdpa_bf16_d128,
                                    wf::attn_table_sdpa_f16_d64,  wf::attn_table_sdpa_f16_d128,
-                                   wf::attn_table_mla,           wf::attn_table_split,
+                                   wf::attn_table_mla,           wf::attn_table_split_bf16,
+                                   wf::attn_table_split_f16,
                                    wf::attn_table_w_bf16_d64,    wf::attn_table_w_bf16_d128,
                                    wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128,
                                    wf::attn_table_p_bf16_d64,    wf::attn_table_p_bf16_d128,
@@ -290,6 +291,39 @@ void visible_range(const wf_block_kv_state* s, int64_t* T, int64_t* head, int64_
 }
 
 constexpr int kMaxSplits = 16;
+
+// Split-KV plan for decode-shaped calls (few queries, long KV): the query heads of a KV group
+// share each K/V tile (hpw heads per work group), and the key tiles are cut into splits so
+// that about kDecodeGroups work groups stream K/V at once. It depends on shapes only, so the
+// workspace size does not depend on the device.
+constexpr int kMaxDecodeSplits = 256;
+constexpr int64_t kDecodeGroups = 512;
+struct DecodePlan {
+  const wf::AttnEntry* e = nullptr;
+  int n_qt = 0, n_splits = 1, tps = 1;
+};
+DecodePlan decode_plan(int dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
+                       int64_t D, int64_t Dv, bool causal) {
+  DecodePlan p;
+  if (Hkv <= 0 || Hq % Hkv != 0) return p;
+  const int64_t G = Hq / Hkv;
+  const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  p.e = find_attn(dt, (int)D, (int)D, (int)Dv, 4, hpw, wf::MASK_NONE, causal ? 1 : 0,
+                  wf::MODE_SPLIT);
+  if (p.e == nullptr) return p;
+  p.n_qt = (int)((Lq + p.e->bmp - 1) / p.e->bmp);
+  const int64_t base = std::max<int64_t>(1, (int64_t)p.n_qt * B * Hkv * (G / hpw));
+  const int64_t n_kt = (Lk + p.e->bn - 1) / p.e->bn;
+  int64_t groups = kDecodeGroups, min_tiles = 2;
+  if (const char* t = getenv("WF_TUNE_DECODE_GROUPS")) groups = std::max(1, atoi(t));
+  if (const char* t = getenv("WF_TUNE_DECODE_MIN_TILES")) min_tiles = std::max(1, atoi(t));
+  int64_t n = (groups + base - 1) / base;
+  n = std::min<int64_t>(n, kMaxDecodeSplits);
+  n = std::min<int64_t>(n, std::max<int64_t>(1, n_kt / min_tiles));  // tiles per split
+  p.tps = (int)std::max<int64_t>(1, (n_kt + n - 1) / n);
+  p.n_splits = (int)std::max<int64_t>(1, (n_kt + p.tps - 1) / p.tps);
+  return p;
+}
 
 }  // namespace
 
@@ -687,7 +721,81 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   if (he != hipSuccess) return hip_status(he, "split attention launch");
   return hip_status(wf::launch_split_combine(dt, a.part_o, a.part_lse, n_splits, (int)B, (int)Hq,
                                              (int)Lq, (int)Dv, out->data, st(out, 0), st(out, 1),
-                                             out->stride[2], strm),
+                                             out->stride[2], nullptr, strm),
+                    "combine launch");
+}
+
+size_t wf_sdpa_decode_workspace_size(const wf_tensor* q, const wf_tensor* k,
+                                     const wf_tensor* v, int is_causal) {
+  if (q == nullptr || k == nullptr || v == nullptr || q->ndim != 4 || k->ndim != 4 || v->ndim != 4)
+    return 0;
+  const DecodePlan p = decode_plan(kernel_dtype(q->dtype), q->shape[0], q->shape[1], k->shape[1],
+                                   q->shape[2], k->shape[2], q->shape[3], v->shape[3],
+                                   is_causal != 0);
+  if (p.e == nullptr) return 0;
+  const int64_t rows = q->shape[0] * q->shape[1] * q->shape[2];
+  return (size_t)((int64_t)p.n_splits * rows * (v->shape[3] + 1) * 4 + 256);
+}
+
+int wf_sdpa_decode(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, int is_causal,
+                   float scale, wf_tensor* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_data(q, "q", 4)) || (rc = check_data(k, "k", 4)) ||
+      (rc = check_data(v, "v", 4)) || (rc = check_data(out, "out", 4)))
+    return rc;
+  if (k->dtype != q->dtype || v->dtype != q->dtype || out->dtype != q->dtype)
+    return fail(WF_ERR_DTYPE, "q, k, v and out must share one dtype");
+  if (q->dtype == WF_F32) return fail(WF_ERR_DTYPE, "decode takes f16 or bf16");
+  const int64_t B = q->shape[0], Hq = q->shape[1], Lq = q->shape[2], D = q->shape[3];
+  const int64_t Hkv = k->shape[1], Lk = k->shape[2], Dv = v->shape[3];
+  if (k->shape[0] != B || v->shape[0] != B || k->shape[3] != D || v->shape[1] != Hkv ||
+      v->shape[2] != Lk)
+    return fail(WF_ERR_SHAPE, "k must be [B,Hkv,Lk,D] and v [B,Hkv,Lk,Dv] for q [B,Hq,Lq,D]");
+  if (out->shape[0] != B || out->shape[1] != Hq || out->shape[2] != Lq || out->shape[3] != Dv)
+    return fail(WF_ERR_SHAPE, "out must be [B,Hq,Lq,Dv]");
+  if (Hkv <= 0 || Hq % Hkv != 0) return fail(WF_ERR_SHAPE, "Hq must be a multiple of Hkv");
+  if (!((D == 64 && Dv == 64) || (D == 128 && Dv == 128)))
+    return fail(WF_ERR_UNSUPPORTED, "head dims (%lld, %lld) not built", (long long)D, (long long)Dv);
+  if (Lq > 0x7fffffff || Lk > 0x7fffffff) return fail(WF_ERR_SHAPE, "sequence length exceeds 2^31");
+  float sc;
+  if ((rc = resolve_scale(scale, D, &sc))) return rc;
+  const int dt = kernel_dtype(q->dtype);
+  const DecodePlan p = decode_plan(dt, B, Hq, Hkv, Lq, Lk, D, Dv, is_causal != 0);
+  if (p.e == nullptr) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
+  const int64_t rows = B * Hq * Lq;
+  const size_t need = (size_t)((int64_t)p.n_splits * rows * (Dv + 1) * 4 + 256);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (rows == 0 || Dv == 0) return ok();
+  const int64_t G = Hq / Hkv;
+  const int64_t base_blocks = (int64_t)p.n_qt * B * Hkv * (G / p.e->hpw);
+  if (base_blocks > 0x7fffffff) return fail(WF_ERR_SHAPE, "problem too large for one launch");
+  wf::FwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q->data; a.q2 = q->data; a.k = k->data; a.k2 = k->data; a.v = v->data;
+  a.o = out->data;
+  a.q_sb = st(q, 0); a.q_sh = st(q, 1); a.q_sm = q->stride[2];
+  a.q2_sb = a.q_sb; a.q2_sh = a.q_sh; a.q2_sm = a.q_sm;
+  a.k_sb = st(k, 0); a.k_sh = st(k, 1); a.k_sm = k->stride[2];
+  a.k2_sb = a.k_sb; a.k2_sh = a.k_sh; a.k2_sm = a.k_sm;
+  a.v_sb = st(v, 0); a.v_sh = st(v, 1); a.v_sm = v->stride[2];
+  a.B = (int)B; a.Hq = (int)Hq; a.Hkv = (int)Hkv; a.G = (int)G; a.Lq = (int)Lq; a.Lk = (int)Lk;
+  a.causal_shift = is_causal ? (int)(Lk - Lq) : 0;   // the queries are the last Lq positions
+  a.n_qtiles = p.n_qt;
+  a.scale_log2 = sc * wf::kLog2e;
+  a.inv_scale = 1.0f / sc;
+  a.tiles_per_split = p.tps;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + (size_t)p.n_splits * rows * Dv * 4);
+  hipStream_t strm = (hipStream_t)stream;
+  hipError_t he = launch(p.e->fn, dim3((unsigned)base_blocks, p.n_splits), dim3(p.e->nw * 64), a, strm);
+  if (he != hipSuccess) return hip_status(he, "split attention launch");
+  return hip_status(wf::launch_split_combine(dt, a.part_o, a.part_lse, p.n_splits, (int)B, (int)Hq,
+                                             (int)Lq, (int)Dv, out->data, st(out, 0), st(out, 1),
+                                             out->stride[2], lse, strm),
                     "combine launch");
 }
 

@@ -26,7 +26,8 @@ const AttnEntry* attn_table_sdpa_bf16_d128(int* n);
 const AttnEntry* attn_table_sdpa_f16_d64(int* n);
 const AttnEntry* attn_table_sdpa_f16_d128(int* n);
 const AttnEntry* attn_table_mla(int* n);
-const AttnEntry* attn_table_split(int* n);
+const AttnEntry* attn_table_split_bf16(int* n);
+const AttnEntry* attn_table_split_f16(int* n);
 const AttnEntry* attn_table_w_bf16_d128(int* n);
 const AttnEntry* attn_table_w_bf16_d64(int* n);
 const AttnEntry* attn_table_w_f16_d128(int* n);
@@ -70,7 +71,8 @@ hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seq
                                   int causal, int max_items, int* ws, hipStream_t s);
 hipError_t launch_split_combine(int dtype, const float* part_o, const float* part_lse,
                                 int n_splits, int B, int Hq, int Lq, int Dv, void* out,
-                                int64_t o_sb, int64_t o_sh, int64_t o_sm, hipStream_t s);
+                                int64_t o_sb, int64_t o_sh, int64_t o_sm, float* lse,
+                                hipStream_t s);
 hipError_t launch_kv_update(int unit, int esize, const void* k_new, const int64_t* kn_st,
                             const void* v_new, const int64_t* vn_st, void* k_cache,
                             const int64_t* kc_st, void* v_cache, const int64_t* vc_st, int B,

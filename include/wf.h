@@ -96,6 +96,26 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
                 wf_tensor* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * wf_sdpa_decode — the same attention as wf_sdpa_fwd for few queries against a long K/V
+ * (decode, and speculative decoding with several new tokens: [MLA] maskType SPEC / calcType
+ * SPEC, q lengths above 1). The key range is split across work groups, each writing an fp32
+ * partial output and log-sum-exp into `workspace`, and a combine kernel merges the splits.
+ *   q [B, Hq, Lq, D], k [B, Hkv, Lk, D], v [B, Hkv, Lk, D], out [B, Hq, Lq, D]; f16 | bf16;
+ *   D in {64, 128}; Hq a multiple of Hkv (GQA as in wf_sdpa_fwd). No mask.
+ *   is_causal: the Lq queries are the last Lq positions of the key sequence (bottom-right:
+ *     query i keeps key j iff j <= i + Lk - Lq) — unlike wf_sdpa_fwd's top-left rule.
+ *   scale as in wf_sdpa_fwd. lse: NULL, or device fp32 [B, Hq, Lq] (natural log).
+ *   workspace: device memory of at least wf_sdpa_decode_workspace_size(q, k, v, is_causal)
+ *     bytes (0 = unsupported shape), 256-byte aligned; its size depends on the shapes only.
+ * Rows that keep no key are 0 (lse -inf). Errors as for wf_sdpa_fwd, plus WF_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------------------- */
+size_t wf_sdpa_decode_workspace_size(const wf_tensor* q, const wf_tensor* k,
+                                     const wf_tensor* v, int is_causal);
+int wf_sdpa_decode(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, int is_causal,
+                   float scale, wf_tensor* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * MLA prefill over a packed variable-length batch ([MLA] definition and parameter table).
  *
  *   q       [nTq, Hq,  Dv]  f16 | bf16 (the value-width "nope" part of the query)
@@ -113,7 +133,9 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
  *           h / (Hq/Hkv)).
  *   qk_scale  multiplies (q . k + q_rope . k_rope); finite and > 0.
  *   mask_type 0 = none (UNDEFINED: an all-zero mask), 1 = causal, aligned bottom-right:
- *           query i of a sequence keeps key j iff j <= i + kv_len - q_len.
+ *           query i of a sequence keeps key j iff j <= i + kv_len - q_len. This also serves
+ *           as the page's MASK_TYPE_SPEC (new tokens at the end of a longer cached sequence,
+ *           q lengths above 1); the page gives that enum no number.
  *   out     [nTq, Hq, Dv], dtype of q. Rows of queries that keep no key are 0.
  *   workspace  device memory of at least
  *           wf_varlen_mla_prefill_workspace_size(batch, nTq, head_num) bytes, 256-byte

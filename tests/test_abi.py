@@ -88,6 +88,31 @@ def test_sdpa_validation_errors(lib):
     assert sdpa(lib, T([0, 8, 16, 128]), T([0, 2, 24, 128]), T([0, 2, 24, 128])) == OK
 
 
+def test_decode_validation_errors(lib):
+    q, k, v = T([2, 8, 1, 128]), T([2, 2, 4096, 128]), T([2, 2, 4096, 128])
+    need = lib.wf_sdpa_decode_workspace_size(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 0)
+    assert need > 256
+    # a shape-only size: the causal variant and a longer K/V give sizes of their own
+    assert lib.wf_sdpa_decode_workspace_size(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 1) > 256
+    assert lib.wf_sdpa_decode_workspace_size(ctypes.byref(T([2, 8, 1, 96])), ctypes.byref(T([2, 2, 64, 96])),
+                                             ctypes.byref(T([2, 2, 64, 96])), 0) == 0
+
+    def call(q=q, k=k, v=v, out=None, causal=0, scale=0.1, ws=FAKE, wsb=need):
+        out = out or T([q.shape[0], q.shape[1], q.shape[2], v.shape[3]], q.dtype)
+        return lib.wf_sdpa_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), causal, scale,
+                                  ctypes.byref(out), None, ws, wsb, None)
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=FAKE + 64) == WS                               # 256-byte alignment
+    assert call(q=T([2, 8, 1, 128], _lib.WF_F32), k=T([2, 2, 4096, 128], _lib.WF_F32),
+                v=T([2, 2, 4096, 128], _lib.WF_F32)) == DTYPE
+    assert call(k=T([2, 3, 4096, 128]), v=T([2, 3, 4096, 128])) == SHAPE   # 8 % 3 != 0
+    assert call(q=T([2, 8, 1, 96]), k=T([2, 2, 64, 96]), v=T([2, 2, 64, 96])) == UNSUP
+    assert call(out=T([2, 8, 2, 128])) == SHAPE
+    assert call(scale=0.0) == UNSUP
+    assert call(q=T([0, 8, 1, 128]), k=T([0, 2, 4096, 128]), v=T([0, 2, 4096, 128])) == OK
+
+
 def test_status_strings(lib):
     assert lib.wf_status_string(0) == b"WF_OK"
     assert lib.wf_status_string(6) == b"WF_ERR_CHUNK_ORDER"
