@@ -103,12 +103,17 @@ struct AttnFwd {
   static constexpr int MSZ = MASK == MASK_BOOL ? 1 : MASK == MASK_HALF ? 2 : 4;
   static constexpr bool MLDS = (MASK == MASK_BOOL || MASK == MASK_HALF) && HPW == 1 && MODE == MODE_DENSE;
   static constexpr int MROWB = BN * MSZ;                 // bytes of one row of a mask tile
+  static constexpr int MCPR = MROWB / 16;                // its 16-byte chunks
+  // chunk swizzle of mask tile rows in LDS (position = chunk ^ mswz(row))
+  static __device__ __forceinline__ int mswz(int row) {
+    return MCPR == 8 ? (row & 7) : MCPR == 4 ? ((row >> 1) & 3) : 0;
+  }
   static constexpr int MBYTES = MLDS ? BMP * MROWB : 16;
   static constexpr int MLOADS = MLDS ? MBYTES / (NT * 16) : 0;
   static_assert(!MLDS || MBYTES % (NT * 16) == 0, "mask tile copies split evenly");
   // K and V tiles of 16 KiB carry the largest alignment, which places them first in LDS
   // (operand reads then address them with immediate offsets).
-  static constexpr int KALIGN = (KBYTES == 16384 && VBYTES == 16384) ? 16384 : 1024;
+  static constexpr int KALIGN = (KBYTES == VBYTES && (KBYTES & (KBYTES - 1)) == 0) ? KBYTES : 1024;
   static_assert(sizeof(T) == 2, "16-bit inputs only");
   static_assert(NW % HPW == 0, "waves split evenly over heads");
   static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile copies split evenly");
@@ -207,7 +212,10 @@ struct AttnFwd {
 
     // Mask tile copies (MLDS): buffer loads with a per-tile descriptor ending after the last
     // valid row's keys; copy i of wave w fills chunks [(i*NW + w)*64, +64) of the tile, lane
-    // -> chunk c, row c / (MROWB/16), byte 16 * (c % (MROWB/16)) of the row.
+    // -> LDS chunk c: row c / MCPR, position c % MCPR, which holds the row's 16-byte chunk
+    // (c % MCPR) ^ mswz(row). Every lane reads its own query row, so unswizzled rows (64 or
+    // 128 bytes apart) would put 16 lanes of a read on one bank; with the swizzle a bool read
+    // is at most 4-way and a 16-bit read 2-way conflicted.
     uint32_t mvo[MLOADS > 0 ? MLOADS : 1];
     const char* mtile0 = nullptr;
     int64_t mrows_bytes = 0;
@@ -216,7 +224,8 @@ struct AttnFwd {
 #pragma unroll
       for (int i = 0; i < MLOADS; ++i) {
         const int c = (i * NW + w) * 64 + lane;
-        mvo[i] = (uint32_t)(c / (MROWB / 16)) * (uint32_t)rs + (uint32_t)(16 * (c % (MROWB / 16)));
+        const int row = c / MCPR;
+        mvo[i] = (uint32_t)row * (uint32_t)rs + (uint32_t)(16 * ((c % MCPR) ^ mswz(row)));
       }
       mtile0 = (const char*)a.mask + (it.b * a.mk_sb + it.hq0 * a.mk_sh + (int64_t)it.pos0 * a.mk_sm) * MSZ;
       const int rows = it.Lq - it.pos0 < BMP ? it.Lq - it.pos0 : BMP;
@@ -300,75 +309,116 @@ struct AttnFwd {
       const int k0 = kt * BN;
       return MASK != MASK_NONE || (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > qlo + it.shift);
     };
-    auto apply_mask = [&](int kt, f32x16* sc) {
-      const int k0 = kt * BN;
-      float mval[2][4][4];
-      if constexpr (MASK != MASK_NONE) {
-        const bool vec = a.mask_vec && (k0 + BN <= it.Lk);
-        const bool lds = MLDS && a.mask_lds;
-        const WF_LDS char* mt = ((kt - it.kt_lo) & 1) ? sM1 : sM0;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int key = k0 + 32 * kb + 8 * q4 + 4 * hf;
-            if (lds) {
-              // this lane's row of the tile (qw + j), keys 32kb + 8q4 + 4hf .. +3
-              const WF_LDS char* src = mt + (qw + j) * MROWB + (32 * kb + 8 * q4 + 4 * hf) * MSZ;
-              if constexpr (MASK == MASK_BOOL) {
-                const uint32_t bits = *reinterpret_cast<const WF_LDS uint32_t*>(src);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  mval[kb][q4][e] = ((bits >> (8 * e)) & 0xffu) ? 0.f : -INFINITY;
-              } else if constexpr (MASK == MASK_HALF) {
-                typedef T t4 __attribute__((ext_vector_type(4)));
-                const t4 hv = *reinterpret_cast<const WF_LDS t4*>(src);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = (float)hv[e];
-              }
-            } else if (vec) {
-              if constexpr (MASK == MASK_BOOL) {
-                const uint32_t bits = *reinterpret_cast<const uint32_t*>(mrow + key);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  mval[kb][q4][e] = ((bits >> (8 * e)) & 0xffu) ? 0.f : -INFINITY;
-              } else if constexpr (MASK == MASK_HALF) {
-                typedef T t4 __attribute__((ext_vector_type(4)));
-                const t4 hv = *reinterpret_cast<const t4*>(mrow + 2 * key);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = (float)hv[e];
-              } else {
-                const f32x4 f4 = *reinterpret_cast<const f32x4*>(mrow + 4 * key);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mval[kb][q4][e] = f4[e];
-              }
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int kk = key + e;
-                float mv = -INFINITY;
-                if (kk < it.Lk) {
-                  if constexpr (MASK == MASK_BOOL) mv = mrow[kk] ? 0.f : -INFINITY;
-                  else if constexpr (MASK == MASK_HALF) mv = (float)reinterpret_cast<const T*>(mrow)[kk];
-                  else mv = reinterpret_cast<const float*>(mrow)[kk];
-                }
-                mval[kb][q4][e] = mv;
-              }
-            }
-          }
-      }
+    int moff[2][4];   // LDS offsets of this lane's mask bytes in a tile (see mswz)
+    if constexpr (MLDS) {
+      const int r = qw + j;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          bool ok = key < it.Lk;
-          if (CAUSAL) ok = ok && key <= qrow + it.shift;
-          float v = sc[kb][r];
-          if constexpr (MASK == MASK_BOOL) v += mval[kb][r >> 2][r & 3];
-          else if constexpr (MASK != MASK_NONE) v += mval[kb][r >> 2][r & 3] * a.inv_scale;
-          sc[kb][r] = ok ? v : -INFINITY;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int byte = (32 * kb + 8 * q4 + 4 * hf) * MSZ;
+          moff[kb][q4] = r * MROWB + (((byte >> 4) ^ mswz(r)) << 4) + (byte & 15);
         }
+    }
+    auto apply_mask = [&](int kt, f32x16* sc) {
+      const int k0 = kt * BN;
+      // Keys past Lk and, for causal calls, keys after the query: only tiles that reach
+      // them need the checks.
+      const bool bounds = (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > qlo + it.shift);
+      if constexpr (MASK != MASK_NONE) {
+        if (MLDS && a.mask_lds) {
+          // This lane's row of the tile (qw + j), keys 32kb + 8q4 + 4hf .. +3, from the LDS
+          // copy (offsets moff, swizzled): every read is issued before the first use, so
+          // the group waits once.
+          const WF_LDS char* mt = ((kt - it.kt_lo) & 1) ? sM1 : sM0;
+          if constexpr (MASK == MASK_BOOL) {
+            uint32_t bits[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4)
+                bits[kb][q4] = *reinterpret_cast<const WF_LDS uint32_t*>(mt + moff[kb][q4]);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                sc[kb][r] = ((bits[kb][r >> 2] >> (8 * (r & 3))) & 0xffu) ? sc[kb][r] : -INFINITY;
+          } else if constexpr (MASK == MASK_HALF) {
+            typedef T t4 __attribute__((ext_vector_type(4)));
+            t4 hv[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4)
+                hv[kb][q4] = *reinterpret_cast<const WF_LDS t4*>(mt + moff[kb][q4]);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                // convert, then an fp32 FMA: the fused mixed-precision FMA measured slower
+                float mv = (float)hv[kb][r >> 2][r & 3];
+                asm volatile("" : "+v"(mv));
+                sc[kb][r] = fmaf(mv, a.inv_scale, sc[kb][r]);
+              }
+          }
+        } else {
+          float mval[2][4][4];
+          const bool vec = a.mask_vec && (k0 + BN <= it.Lk);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int key = k0 + 32 * kb + 8 * q4 + 4 * hf;
+              if (vec) {
+                if constexpr (MASK == MASK_BOOL) {
+                  const uint32_t bits = *reinterpret_cast<const uint32_t*>(mrow + key);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    mval[kb][q4][e] = ((bits >> (8 * e)) & 0xffu) ? 0.f : -INFINITY;
+                } else if constexpr (MASK == MASK_HALF) {
+                  typedef T t4 __attribute__((ext_vector_type(4)));
+                  const t4 hv = *reinterpret_cast<const t4*>(mrow + 2 * key);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) mval[kb][q4][e] = (float)hv[e];
+                } else {
+                  const f32x4 f4 = *reinterpret_cast<const f32x4*>(mrow + 4 * key);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) mval[kb][q4][e] = f4[e];
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int kk = key + e;
+                  float mv = -INFINITY;
+                  if (kk < it.Lk) {
+                    if constexpr (MASK == MASK_BOOL) mv = mrow[kk] ? 0.f : -INFINITY;
+                    else if constexpr (MASK == MASK_HALF) mv = (float)reinterpret_cast<const T*>(mrow)[kk];
+                    else mv = reinterpret_cast<const float*>(mrow)[kk];
+                  }
+                  mval[kb][q4][e] = mv;
+                }
+              }
+            }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if constexpr (MASK == MASK_BOOL) sc[kb][r] += mval[kb][r >> 2][r & 3];
+              else sc[kb][r] = fmaf(mval[kb][r >> 2][r & 3], a.inv_scale, sc[kb][r]);
+            }
+        }
+      }
+      if (bounds) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            bool ok = key < it.Lk;
+            if (CAUSAL) ok = ok && key <= qrow + it.shift;
+            sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
+          }
+      }
     };
 
     // ---- pipeline pieces -------------------------------------------------------------------
