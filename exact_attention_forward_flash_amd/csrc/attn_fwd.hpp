@@ -106,7 +106,7 @@ struct AttnFwd {
   static constexpr int MCPR = MROWB / 16;                // its 16-byte chunks
   // chunk swizzle of mask tile rows in LDS (position = chunk ^ mswz(row))
   static __device__ __forceinline__ int mswz(int row) {
-    return MCPR == 8 ? (row & 7) : MCPR == 4 ? ((row >> 1) & 3) : 0;
+    return ((row >> 1) ^ (row >> 3)) & (MCPR - 1);
   }
   static constexpr int MBYTES = MLDS ? BMP * MROWB : 16;
   static constexpr int MLOADS = MLDS ? MBYTES / (NT * 16) : 0;
@@ -214,8 +214,9 @@ struct AttnFwd {
     // valid row's keys; copy i of wave w fills chunks [(i*NW + w)*64, +64) of the tile, lane
     // -> LDS chunk c: row c / MCPR, position c % MCPR, which holds the row's 16-byte chunk
     // (c % MCPR) ^ mswz(row). Every lane reads its own query row, so unswizzled rows (64 or
-    // 128 bytes apart) would put 16 lanes of a read on one bank; with the swizzle a bool read
-    // is at most 4-way and a 16-bit read 2-way conflicted.
+    // 128 bytes apart) would put 16 lanes of a read on one bank. With the swizzle, bool
+    // masks (read as whole chunks) are conflict-free and 16-bit masks (8-byte reads) 2-way,
+    // whether the LDS serves 128 or 256 bytes per clock.
     uint32_t mvo[MLOADS > 0 ? MLOADS : 1];
     const char* mtile0 = nullptr;
     int64_t mrows_bytes = 0;
@@ -309,14 +310,16 @@ struct AttnFwd {
       const int k0 = kt * BN;
       return MASK != MASK_NONE || (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > qlo + it.shift);
     };
-    int moff[2][4];   // LDS offsets of this lane's mask bytes in a tile (see mswz)
+    // LDS offsets of this lane's mask bytes in a tile (see mswz): 16-bit masks, the 8 bytes
+    // of keys 32kb + 8q4 + 4hf .. +3; bool masks, the whole chunks 2kb + q4/2 (q4 even).
+    int moff[2][4];
     if constexpr (MLDS) {
       const int r = qw + j;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int byte = (32 * kb + 8 * q4 + 4 * hf) * MSZ;
+          const int byte = MASK == MASK_BOOL ? 32 * kb + 16 * (q4 >> 1) : (32 * kb + 8 * q4 + 4 * hf) * MSZ;
           moff[kb][q4] = r * MROWB + (((byte >> 4) ^ mswz(r)) << 4) + (byte & 15);
         }
     }
@@ -332,12 +335,21 @@ struct AttnFwd {
           // the group waits once.
           const WF_LDS char* mt = ((kt - it.kt_lo) & 1) ? sM1 : sM0;
           if constexpr (MASK == MASK_BOOL) {
+            // chunk 2kb + h holds keys 32kb + 16h .. +15; this lane's 4-key groups q4 = 2h,
+            // 2h + 1 are its dwords hf and 2 + hf
+            u32x4 ch[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) ch[kb][h] = lds_read16(mt + moff[kb][2 * h]);
             uint32_t bits[2][4];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int q4 = 0; q4 < 4; ++q4)
-                bits[kb][q4] = *reinterpret_cast<const WF_LDS uint32_t*>(mt + moff[kb][q4]);
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const u32x4 v = ch[kb][q4 >> 1];
+                bits[kb][q4] = (q4 & 1) ? (hf ? v[3] : v[2]) : (hf ? v[1] : v[0]);
+              }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
