@@ -689,7 +689,11 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
   const int64_t base_blocks = (int64_t)n_qt * B * Hq;
   const int cus = device_cus();
-  int n_splits = (int)((2 * cus + base_blocks - 1) / base_blocks);
+  // About one work group per CU: measured on the 256-query chunk over a 4k window, 192-384
+  // groups run 20% faster than 512 (fewer fp32 partials to write and merge).
+  int64_t target = cus;
+  if (const char* t = getenv("WF_TUNE_ATTEND_GROUPS")) target = std::max(1, atoi(t));
+  int n_splits = (int)((target + base_blocks - 1) / base_blocks);
   if (n_splits > kMaxSplits) n_splits = kMaxSplits;
   if (n_splits > n_kt) n_splits = n_kt;
   if (n_splits <= 1)
