@@ -14,11 +14,13 @@ Sources (the pages this project implements):
   * Huawei Ascend CANN ATB page "MLA Prefill": the definition of
     AtbMLAPreFillGetWorkspaceSize and its parameter table (Q/QRope/K/kRope/V layouts,
     qSeqLen/kvSeqLen, headNum, kvHeadNum, qkScale, maskType).
+  * "Core 注意力", the responsibility list at its top (the core applies RoPE): oracle.rotary.
 
 Parity status of every function is stated in its module header.
 """
 from .attention import sdpa, varlen_mla_prefill, cu_seqlens
 from .block_kv_cache import BlockKVCacheOracle, CacheOrderError, CacheConfigError
+from .rotary import rope, sdpa_rope
 
 __all__ = ["sdpa", "varlen_mla_prefill", "cu_seqlens", "BlockKVCacheOracle",
-           "CacheOrderError", "CacheConfigError"]
+           "CacheOrderError", "CacheConfigError", "rope", "sdpa_rope"]

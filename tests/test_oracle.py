@@ -374,3 +374,70 @@ def _expected_cache_walk(sink, window, chunk, steps, seed):
     if (s + w) % ch == 0 and w >= ch and s + w <= 16])
 def test_cache_walk_invariants(sink, window, chunk):
     _expected_cache_walk(sink, window, chunk, steps=14, seed=sink * 100 + window * 10 + chunk)
+
+
+# ---------------------------------------------------------------- rotary embedding ----
+
+from oracle.rotary import rope, sdpa_rope, INTERLEAVED, ROTATE_HALF
+
+
+def _tables(max_pos, rot_dim, base=10000.0):
+    theta = base ** (-np.arange(rot_dim // 2) * 2.0 / rot_dim)
+    ang = np.arange(max_pos)[:, None] * theta[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def test_rope_single_pair_is_a_plane_rotation():
+    # one pair at one position: the 2-d rotation matrix by that angle
+    for style in (ROTATE_HALF, INTERLEAVED):
+        x = np.array([[[0.3, -1.2]]])
+        phi = 0.7
+        out = rope(x, np.array([[np.cos(phi)]] * 2), np.array([[np.sin(phi)]] * 2), 2, style, pos0=1)
+        rot = np.array([[np.cos(phi), -np.sin(phi)], [np.sin(phi), np.cos(phi)]])
+        np.testing.assert_allclose(out[0, 0], rot @ x[0, 0], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("style", [ROTATE_HALF, INTERLEAVED])
+def test_rope_preserves_norms_and_the_tail(style):
+    x = _t((2, 3, 17, 24), 5).numpy().astype(np.float64)
+    c, s = _tables(40, 16)
+    out = rope(x, c, s, 16, style, pos0=7)
+    np.testing.assert_allclose(np.linalg.norm(out, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-12)
+    np.testing.assert_array_equal(out[..., 16:], x[..., 16:])     # dims past rot_dim unchanged
+    assert np.abs(out[..., :16] - x[..., :16]).max() > 1e-2       # and the rest did move
+    np.testing.assert_array_equal(rope(x, c, s, 0, style), x)     # rot_dim 0: identity
+
+
+@pytest.mark.parametrize("style", [ROTATE_HALF, INTERLEAVED])
+def test_rope_scores_depend_on_distance_only(style):
+    # with tables cos(p*theta), sin(p*theta) the rotated q_m . k_n is a function of m - n
+    q = _t((1, 2, 5, 32), 6).numpy().astype(np.float64)
+    k = _t((1, 2, 5, 32), 7).numpy().astype(np.float64)
+    c, s = _tables(64, 32)
+    a = rope(q, c, s, 32, style, 3) @ rope(k, c, s, 32, style, 0).swapaxes(-1, -2)
+    b = rope(q, c, s, 32, style, 40) @ rope(k, c, s, 32, style, 37).swapaxes(-1, -2)
+    np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-10)
+    # and not an invariant of everything: a different distance changes the scores
+    d = rope(q, c, s, 32, style, 41) @ rope(k, c, s, 32, style, 37).swapaxes(-1, -2)
+    assert np.abs(a - d).max() > 1e-3
+
+
+def test_rope_styles_differ_by_a_permutation_of_dims():
+    x = _t((1, 1, 6, 8), 8).numpy().astype(np.float64)
+    c, s = _tables(10, 8)
+    perm = np.array([0, 4, 1, 5, 2, 6, 3, 7])          # interleaved position -> half position
+    half = rope(x[..., perm], c, s, 8, INTERLEAVED, 2)  # dims 2i, 2i+1 hold i, i+4
+    np.testing.assert_allclose(half[..., np.argsort(perm)], rope(x, c, s, 8, ROTATE_HALF, 2),
+                               rtol=0, atol=1e-14)
+
+
+def test_sdpa_rope_equals_sdpa_of_rotated_inputs():
+    q, k, v = _t((2, 4, 9, 16), 9), _t((2, 2, 11, 16), 10), _t((2, 2, 11, 8), 11)
+    c, s = _tables(32, 12)
+    out, lse = sdpa_rope(q, k, v, c, s, 12, ROTATE_HALF, q_pos0=2, k_pos0=0, is_causal=True)
+    qr = torch.from_numpy(rope(q, c, s, 12, ROTATE_HALF, 2))
+    kr = torch.from_numpy(rope(k, c, s, 12, ROTATE_HALF, 0))
+    ref = _torch_sdpa(qr, kr, v.double(), is_causal=True)
+    np.testing.assert_allclose(out, ref, **TIGHT)
+    with pytest.raises(ValueError):
+        rope(q, c, s, 12, ROTATE_HALF, pos0=30)        # positions past the tables

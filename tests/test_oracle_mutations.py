@@ -12,6 +12,7 @@ import pytest
 
 import oracle.attention as oa
 import oracle.block_kv_cache as ob
+import oracle.rotary as orope
 from tests import test_oracle as pins
 
 MUTATIONS = [
@@ -29,6 +30,10 @@ MUTATIONS = [
     ("attention", "kg, krg, vg = ki[:, g], kri[:, g], vi[:, g]", "kg, krg, vg = ki[:, 0], kri[:, g], vi[:, g]", "MLA kv head fixed"),
     ("attention", "return k[i, :lk_i], kr[i, :lk_i], v[i, :lk_i]", "return k[0, :lk_i], kr[i, :lk_i], v[i, :lk_i]", "padded K of the wrong batch entry"),
     ("attention", "return k[i, :lk_i], kr[i, :lk_i], v[i, :lk_i]", "return k[i, :lk_i], kr[i, :lk_i], v[i, 1:lk_i + 1]", "padded V rows shifted"),
+    ("rope", "x[..., b] = xb * c + xa * s", "x[..., b] = xb * c - xa * s", "rotation sign"),
+    ("rope", "c = cos[pos0:pos0 + L, :rot_dim // 2]", "c = cos[0:L, :rot_dim // 2]", "cos position offset dropped"),
+    ("rope", "return np.arange(h), np.arange(h) + h", "return np.arange(h), np.arange(h) + 1", "rotate-half pairing"),
+    ("rope", "rope(k, cos, sin, rot_dim, style, k_pos0)", "rope(k, cos, sin, rot_dim, style, q_pos0)", "key positions"),
     ("block_kv_cache", "max(self.sink, T - self.window)", "max(0, T - self.window)", "window start ignores sink"),
     ("block_kv_cache", "(self.last_chunk, self.last_chunk + 1)", "(self.last_chunk, self.last_chunk + 1, self.last_chunk + 2)", "skip allowed"),
     ("block_kv_cache", "min(T, self.sink)", "min(T, self.sink + 1)", "sink length"),
@@ -37,8 +42,8 @@ MUTATIONS = [
 
 
 def _mutated_module(which, old, new):
-    mod = oa if which == "attention" else ob
-    src = inspect.getsource(mod)
+    mod = {"attention": oa, "block_kv_cache": ob, "rope": orope}[which]
+    src = inspect.getsource(mod).replace("from .attention import", "from oracle.attention import")
     assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
     src = src.replace(old, new)
     m = types.ModuleType(f"mutant_{which}")
@@ -77,6 +82,9 @@ def test_planted_mistake_fails_a_pin(monkeypatch, which, old, new, what):
     if which == "attention":
         monkeypatch.setattr(pins, "sdpa", m.sdpa)
         monkeypatch.setattr(pins, "varlen_mla_prefill", m.varlen_mla_prefill)
+    elif which == "rope":
+        monkeypatch.setattr(pins, "rope", m.rope)
+        monkeypatch.setattr(pins, "sdpa_rope", m.sdpa_rope)
     else:
         monkeypatch.setattr(pins, "BlockKVCacheOracle", m.BlockKVCacheOracle)
         monkeypatch.setattr(pins, "CacheOrderError", m.CacheOrderError)
