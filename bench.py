@@ -205,6 +205,23 @@ def other_workload(name, steps, warmup):
                     update_gbs=round(upd_bytes * reps / (tot_u * 1e-3) / 1e9, 1),
                     attend_ms_per_chunk=round(tot_a / reps / n, 4),
                     attend_tflops=round(fl / (tot_a * 1e-3) / 1e12, 2))
+    elif name == "rope_gqa":
+        import numpy as np
+        w = synth.causal_gqa_prefill()
+        q, k, v = (w[n].to(dev) for n in ("q", "k", "v"))
+        theta = 10000.0 ** (-np.arange(64) * 2.0 / 128)
+        ang = np.arange(4096)[:, None] * theta[None, :]
+        c = torch.from_numpy(np.cos(ang)).float().to(dev)
+        sn = torch.from_numpy(np.sin(ang)).float().to(dev)
+        ws = torch.empty(2 * (q.numel() + k.numel()) + 1024, dtype=torch.uint8, device=dev)
+        ms = _time_steps(lambda: wf.sdpa_rope(q, k, v, c, sn, 128, 0, is_causal=True,
+                                               scale=w["scale"], workspace=ws), steps, warmup, stream)
+        ms0 = _time_steps(lambda: wf.sdpa(q, k, v, is_causal=True, scale=w["scale"]), steps, warmup,
+                          stream)
+        fl = flops_per_step(4, 32, 4096, 128, True)
+        line.update(ms=round(ms, 4), tflops=round(fl / ms / 1e9, 2), sdpa_ms=round(ms0, 4),
+                    rope_pass_ms=round(ms - ms0, 4),
+                    rope_pass_gbs=round(2 * (q.numel() + k.numel()) * 2 / ((ms - ms0) * 1e-3) / 1e9, 1))
     elif name == "decode":
         B, Hq, Hkv, Lk, D = 8, 32, 8, 16384, 128
         w = synth.random_sdpa_inputs(B, Hq, Hkv, 1, Lk, D, D, "bf16", seed=7)
@@ -235,7 +252,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="causal_gqa",
                     choices=["causal_gqa", "varlen_mla", "masked_bool", "masked_float",
-                             "cache_stream", "page_example", "decode"],
+                             "cache_stream", "page_example", "decode", "rope_gqa"],
                     help="causal_gqa (default) prints the headline line; the others time one of "
                          "the other configurations and print its kernel throughput")
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",

@@ -27,6 +27,12 @@ class WfBlockKvState(ctypes.Structure):
                 ("last_chunk", ctypes.c_int64)]
 
 
+class WfRope(ctypes.Structure):
+    _fields_ = [("cos", ctypes.c_void_p), ("sin", ctypes.c_void_p), ("max_pos", ctypes.c_int64),
+                ("rot_dim", ctypes.c_int), ("style", ctypes.c_int), ("q_pos0", ctypes.c_int64),
+                ("k_pos0", ctypes.c_int64)]
+
+
 _T = ctypes.POINTER(WfTensor)
 _S = ctypes.POINTER(WfBlockKvState)
 _vp, _i32, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -34,6 +40,9 @@ _vp, _i32, _i64, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes
 # name -> (restype, argtypes); the full exported surface of include/wf.h
 SIGNATURES = {
     "wf_sdpa_fwd": (_i32, [_T, _T, _T, _T, _i32, _f, _f, _T, ctypes.POINTER(ctypes.c_float), _vp]),
+    "wf_sdpa_rope_workspace_size": (_sz, [_T, _T]),
+    "wf_sdpa_rope_fwd": (_i32, [_T, _T, _T, _T, _i32, _f, ctypes.POINTER(WfRope), _T,
+                                ctypes.POINTER(ctypes.c_float), _vp, _sz, _vp]),
     "wf_sdpa_decode_workspace_size": (_sz, [_T, _T, _T, _i32]),
     "wf_sdpa_decode": (_i32, [_T, _T, _T, _i32, _f, _T, ctypes.POINTER(ctypes.c_float), _vp, _sz,
                               _vp]),

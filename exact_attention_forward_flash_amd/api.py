@@ -65,6 +65,30 @@ def sdpa(q, k, v, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
     return (out, lse) if return_lse else out
 
 
+def sdpa_rope(q, k, v, cos, sin, rot_dim=None, style=0, q_pos0=0, k_pos0=0, attn_mask=None,
+              is_causal=False, scale=None, return_lse=False, workspace=None):
+    """sdpa() with rotary position embedding on q and k: cos/sin fp32 [max_pos, rot_dim/2]
+    device tables (pair i of a row at position p turns by cos[p, i], sin[p, i]); style 0 pairs
+    (i, i + rot_dim/2), style 1 pairs (2i, 2i + 1); query row r sits at q_pos0 + r, key row j at
+    k_pos0 + j. rot_dim defaults to 2 * cos.shape[1]."""
+    lib = _lib.load()
+    cos, sin = cos.contiguous(), sin.contiguous()
+    rot = 2 * cos.shape[1] if rot_dim is None else int(rot_dim)
+    out = torch.empty(q.shape[:3] + (v.shape[3],), dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    dq, dk, dv, dm, do = describe(q), describe(k), describe(v), describe(attn_mask), describe(out)
+    need = int(lib.wf_sdpa_rope_workspace_size(_ref(dq), _ref(dk)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    r = _lib.WfRope(cos.data_ptr(), sin.data_ptr(), cos.shape[0], rot, int(style), int(q_pos0),
+                    int(k_pos0))
+    lse_ptr = ctypes.cast(lse.data_ptr(), ctypes.POINTER(ctypes.c_float)) if lse is not None and lse.numel() else None
+    check(lib.wf_sdpa_rope_fwd(_ref(dq), _ref(dk), _ref(dv), _ref(dm), int(bool(is_causal)),
+                               _scale(scale), ctypes.byref(r), _ref(do), lse_ptr,
+                               ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
 def sdpa_decode_workspace_size(q, k, v, is_causal=False):
     return int(_lib.load().wf_sdpa_decode_workspace_size(_ref(describe(q)), _ref(describe(k)),
                                                          _ref(describe(v)), int(bool(is_causal))))

@@ -347,9 +347,18 @@ const char* wf_status_string(int status) {
 
 const char* wf_last_error(void) { return g_last_error.c_str(); }
 
-int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
-                const wf_tensor* mask, int is_causal, float dropout_p, float scale,
-                wf_tensor* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+// The checks of wf_sdpa_fwd (nothing enqueued); on success *plan holds what run_dense needs.
+struct SdpaPlan {
+  int mask_kind = wf::MASK_NONE;
+  bool mask_vec = false, mask_lds = false, empty = false;
+  float scale = 0.f;
+};
+int sdpa_validate(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
+                  const wf_tensor* mask, int is_causal, float dropout_p, float scale,
+                  const wf_tensor* out, const float* lse, SdpaPlan* plan) {
   int rc;
   if ((rc = check_data(q, "q", 4)) || (rc = check_data(k, "k", 4)) ||
       (rc = check_data(v, "v", 4)) || (rc = check_data(out, "out", 4)))
@@ -372,8 +381,7 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
     return fail(WF_ERR_UNSUPPORTED, "dropout_p must be 0 (inference forward only)");
   if (mask && is_causal)
     return fail(WF_ERR_UNSUPPORTED, "a mask together with is_causal is not accepted");
-  float sc;
-  if ((rc = resolve_scale(scale, Dqk, &sc))) return rc;
+  if ((rc = resolve_scale(scale, Dqk, &plan->scale))) return rc;
   const bool f32 = q->dtype == WF_F32;
   if (f32 ? !((Dqk == 64 || Dqk == 128) && (Dv == 64 || Dv == 96 || Dv == 128))
           : !((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128)))
@@ -381,8 +389,9 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
                 (long long)Dqk, (long long)Dv);
   if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(WF_ERR_LAYOUT, "lse must be 4-byte aligned");
-  int mask_kind = wf::MASK_NONE;
-  bool mask_vec = false, mask_lds = false;
+  int& mask_kind = plan->mask_kind;
+  bool& mask_vec = plan->mask_vec;
+  bool& mask_lds = plan->mask_lds;
   if (mask) {
     if (mask->ndim != 4) return fail(WF_ERR_SHAPE, "mask must be 4-d [B|1, Hq|1, Lq, Lk]");
     const int64_t want[4] = {B, Hq, Lq, Lk};
@@ -411,9 +420,93 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
         if (mask->shape[i] > 1 && (mask->stride[i] * ms) % 16 != 0) mask_lds = false;
     }
   }
-  if (B * Hq * Lq == 0 || Dv == 0) return ok();
-  return run_dense(q, k, v, mask, mask_kind, mask_vec, mask_lds, is_causal ? 1 : 0, sc, out, lse,
-                   Lk, (hipStream_t)stream);
+  plan->empty = B * Hq * Lq == 0 || Dv == 0;
+  return WF_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
+                const wf_tensor* mask, int is_causal, float dropout_p, float scale,
+                wf_tensor* out, float* lse, void* stream) {
+  SdpaPlan p;
+  int rc = sdpa_validate(q, k, v, mask, is_causal, dropout_p, scale, out, lse, &p);
+  if (rc) return rc;
+  if (p.empty) return ok();
+  return run_dense(q, k, v, mask, p.mask_kind, p.mask_vec, p.mask_lds, is_causal ? 1 : 0, p.scale,
+                   out, lse, k->shape[2], (hipStream_t)stream);
+}
+
+static int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+size_t wf_sdpa_rope_workspace_size(const wf_tensor* q, const wf_tensor* k) {
+  if (q == nullptr || k == nullptr || q->ndim != 4 || k->ndim != 4) return 0;
+  for (int i = 0; i < 4; ++i)
+    if (q->shape[i] < 0 || k->shape[i] < 0) return 0;
+  const int64_t es = esize(q->dtype);
+  return (size_t)(align256(numel(q) * es) + align256(numel(k) * es) + 256);
+}
+
+int wf_sdpa_rope_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
+                     const wf_tensor* mask, int is_causal, float scale, const wf_rope* rope,
+                     wf_tensor* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  SdpaPlan p;
+  int rc = sdpa_validate(q, k, v, mask, is_causal, 0.f, scale, out, lse, &p);
+  if (rc) return rc;
+  if (rope == nullptr) return fail(WF_ERR_NULL, "rope is NULL");
+  const int64_t Lq = q->shape[2], Lk = k->shape[2], D = q->shape[3];
+  const int rot = rope->rot_dim;
+  if (rot < 0 || rot > D || rot % 16 != 0)
+    return fail(WF_ERR_UNSUPPORTED, "rot_dim must be a multiple of 16 in [0, %lld]", (long long)D);
+  if (rope->style != 0 && rope->style != 1)
+    return fail(WF_ERR_UNSUPPORTED, "rope style must be 0 (rotate-half) or 1 (interleaved)");
+  if (rot > 0) {
+    if (rope->cos == nullptr || rope->sin == nullptr) return fail(WF_ERR_NULL, "rope tables are NULL");
+    if (reinterpret_cast<uintptr_t>(rope->cos) % 16 != 0 || reinterpret_cast<uintptr_t>(rope->sin) % 16 != 0)
+      return fail(WF_ERR_LAYOUT, "rope tables must be 16-byte aligned");
+    if (rope->q_pos0 < 0 || rope->k_pos0 < 0 || rope->q_pos0 + Lq > rope->max_pos ||
+        rope->k_pos0 + Lk > rope->max_pos)
+      return fail(WF_ERR_SHAPE, "positions [%lld, %lld) and [%lld, %lld) must lie in the %lld table rows",
+                  (long long)rope->q_pos0, (long long)(rope->q_pos0 + Lq), (long long)rope->k_pos0,
+                  (long long)(rope->k_pos0 + Lk), (long long)rope->max_pos);
+  }
+  const size_t need = wf_sdpa_rope_workspace_size(q, k);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(WF_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (p.empty) return ok();
+  if (rot == 0)
+    return run_dense(q, k, v, mask, p.mask_kind, p.mask_vec, p.mask_lds, is_causal ? 1 : 0, p.scale,
+                     out, lse, Lk, (hipStream_t)stream);
+  // rotated copies, contiguous [B, H, L, D], in the workspace
+  const int64_t es = esize(q->dtype);
+  wf_tensor qr = *q, kr = *k;
+  qr.data = workspace;
+  kr.data = (char*)workspace + align256(numel(q) * es);
+  for (wf_tensor* t : {&qr, &kr}) {
+    t->stride[3] = 1;
+    t->stride[2] = t->shape[3];
+    t->stride[1] = t->shape[2] * t->stride[2];
+    t->stride[0] = t->shape[1] * t->stride[1];
+  }
+  auto desc = [&](const wf_tensor* t, const wf_tensor* o, int64_t pos0) {
+    wf::RopeDesc d;
+    d.x = t->data; d.sb = st(t, 0); d.sh = st(t, 1); d.sm = t->stride[2];
+    d.y = o->data;
+    d.B = (int)t->shape[0]; d.H = (int)t->shape[1]; d.L = (int)t->shape[2];
+    d.pos0 = pos0;
+    return d;
+  };
+  hipStream_t strm = (hipStream_t)stream;
+  hipError_t he = wf::launch_rope(kernel_dtype(q->dtype), desc(q, &qr, rope->q_pos0),
+                                  desc(k, &kr, rope->k_pos0), (int)D, rot, rope->style, rope->cos,
+                                  rope->sin, strm);
+  if (he != hipSuccess) return hip_status(he, "rope launch");
+  return run_dense(&qr, &kr, v, mask, p.mask_kind, p.mask_vec, p.mask_lds, is_causal ? 1 : 0,
+                   p.scale, out, lse, Lk, strm);
 }
 
 size_t wf_varlen_mla_prefill_workspace_size(int batch, int64_t total_q_tokens, int head_num) {

@@ -65,6 +65,18 @@ struct F32Entry {
 };
 const F32Entry* attn_table_f32(int* n);
 
+// Rotary embedding pass (rope.hip): one tensor's input strides, contiguous output, shape and
+// first position.
+struct RopeDesc {
+  const void* x;
+  int64_t sb, sh, sm;
+  void* y;
+  int B, H, L;
+  int64_t pos0;
+};
+hipError_t launch_rope(int dtype, const RopeDesc& q, const RopeDesc& k, int D, int rot, int style,
+                       const float* cosb, const float* sinb, hipStream_t st);
+
 // Auxiliary kernels.
 hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
                                   int64_t total_q, int64_t total_k, int max_kv, int bmp, int bn,

@@ -96,6 +96,35 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
                 wf_tensor* out, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * wf_sdpa_rope_fwd — wf_sdpa_fwd with rotary position embedding applied to q and k first
+ * ([CORE] opening paragraph: applying RoPE is one of the core's jobs; no convention is given).
+ * The first rot_dim dims of every q and k head turn pairwise: pair i of a row at position p
+ * by cos[p * rot_dim/2 + i], sin[...] (caller-tabulated, so any frequency schedule works):
+ *   (x_a, x_b) -> (x_a cos - x_b sin, x_b cos + x_a sin),
+ * pairs (i, i + rot_dim/2) for style 0 (rotate-half) or (2i, 2i + 1) for style 1
+ * (interleaved). Query row r sits at position q_pos0 + r, key row j at k_pos0 + j; v is not
+ * rotated. One launch writes rotated contiguous copies of q and k into `workspace`, then the
+ * attention of wf_sdpa_fwd runs on them (same masks, causal rule, lse, dtypes, head dims).
+ *   rope->cos, rope->sin  device fp32 [max_pos, rot_dim/2], contiguous, 16-byte aligned;
+ *   rot_dim 0 (no rotation) or a multiple of 16 up to the head dim; positions must lie in the
+ *   table. workspace: at least wf_sdpa_rope_workspace_size(q, k) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------------------- */
+typedef struct {
+  const float* cos;
+  const float* sin;
+  int64_t max_pos;
+  int rot_dim;
+  int style;
+  int64_t q_pos0, k_pos0;
+} wf_rope;
+
+size_t wf_sdpa_rope_workspace_size(const wf_tensor* q, const wf_tensor* k);
+int wf_sdpa_rope_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
+                     const wf_tensor* mask, int is_causal, float scale, const wf_rope* rope,
+                     wf_tensor* out, float* lse, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * wf_sdpa_decode — the same attention as wf_sdpa_fwd for few queries against a long K/V
  * (decode, and speculative decoding with several new tokens: [MLA] maskType SPEC / calcType
  * SPEC, q lengths above 1). The key range is split across work groups, each writing an fp32

@@ -119,6 +119,9 @@ WORKLOADS = {
     "masked_float": dict(desc="masked SDPA, fp16, B=2 H=16 L=2048 d=64, additive mask"),
     "cache_stream": dict(desc="rolling block KV cache, fp16, 24 heads d=128, chunk 256, "
                               "sink 256 + window 3840, 64 chunks"),
+    "rope_gqa": dict(desc="causal GQA prefill with rotate-half RoPE over all 128 dims (cos/sin "
+                          "tables of base 10000), bf16, B=4 Hq=32 Hkv=8 L=4096 (beyond the five "
+                          "configurations)"),
     "decode": dict(desc="GQA decode, bf16, B=8 Hq=32 Hkv=8, 1 query over 16384 keys, d=128 "
                         "(split-KV; beyond the five configurations)"),
 }

@@ -113,6 +113,33 @@ def test_decode_validation_errors(lib):
     assert call(q=T([0, 8, 1, 128]), k=T([0, 2, 4096, 128]), v=T([0, 2, 4096, 128])) == OK
 
 
+def test_rope_validation_errors(lib):
+    q, k, v = T([1, 4, 16, 128]), T([1, 2, 24, 128]), T([1, 2, 24, 128])
+    out = T([1, 4, 16, 128])
+    need = lib.wf_sdpa_rope_workspace_size(ctypes.byref(q), ctypes.byref(k))
+    assert need >= (4 * 16 + 2 * 24) * 128 * 2   # rotated copies of q and k
+
+    def call(rot=64, style=0, qp=0, kp=0, max_pos=64, cos=FAKE, ws=FAKE, wsb=need, rope=True, q=q, k=k, v=v,
+             out=out):
+        r = _lib.WfRope(cos, FAKE, max_pos, rot, style, qp, kp)
+        return lib.wf_sdpa_rope_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None, 0, 0.1,
+                                    ctypes.byref(r) if rope else None, ctypes.byref(out), None,
+                                    ws, wsb, None)
+    assert call(rope=False) == NULL
+    assert call(rot=40) == UNSUP                      # not a multiple of 16
+    assert call(rot=144) == UNSUP                     # past the head dim
+    assert call(style=2) == UNSUP
+    assert call(cos=None) == NULL
+    assert call(cos=FAKE + 4) == LAYOUT               # 16-byte aligned tables
+    assert call(qp=50) == SHAPE                       # q positions 50..65 past 64 rows
+    assert call(kp=-1) == SHAPE
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(k=T([1, 3, 24, 128]), v=T([1, 3, 24, 128])) == SHAPE   # SDPA checks come first
+    assert call(q=T([0, 4, 16, 128]), k=T([0, 2, 24, 128]), v=T([0, 2, 24, 128]),
+                out=T([0, 4, 16, 128])) == OK   # empty: validated, nothing launched
+
+
 def test_status_strings(lib):
     assert lib.wf_status_string(0) == b"WF_OK"
     assert lib.wf_status_string(6) == b"WF_ERR_CHUNK_ORDER"

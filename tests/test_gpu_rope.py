@@ -1,0 +1,105 @@
+"""GPU parity of wf_sdpa_rope_fwd (rotary embedding on q and k, then attention) against the
+fp64 oracle, and of the [B, S, hidden] layouts (heads split out by strides) against [B, H, S, D]."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_forward_flash_amd import WfError, sdpa, sdpa_rope
+from synth import causal_gqa_prefill, random_sdpa_inputs
+from tests.parity import assert_close, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _tables(max_pos, rot, base=10000.0):
+    """cos / sin of p * theta_i, theta_i = base^(-2i/rot), computed in fp64, stored fp32."""
+    theta = base ** (-np.arange(rot // 2) * 2.0 / rot)
+    ang = np.arange(max_pos)[:, None] * theta[None, :]
+    return (torch.from_numpy(np.cos(ang)).float(), torch.from_numpy(np.sin(ang)).float())
+
+
+CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, rot, style, q_pos0, k_pos0, causal
+    ("bf16", 2, 8, 2, 130, 130, 128, 128, 0, 0, 0, True),
+    ("bf16", 1, 4, 4, 77, 300, 128, 64, 1, 223, 0, False),   # cached prefix: queries later
+    ("fp16", 2, 6, 3, 257, 257, 64, 64, 0, 5, 5, True),
+    ("fp16", 1, 2, 1, 33, 1000, 64, 32, 1, 0, 0, False),
+    ("fp32", 2, 4, 2, 40, 70, 64, 48, 0, 3, 0, False),
+    ("bf16", 1, 8, 8, 300, 300, 128, 0, 0, 0, 0, True),      # rot 0: plain attention
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
+def test_rope_shapes(case):
+    dt, B, Hq, Hkv, Lq, Lk, D, rot, style, qp, kp, causal = case
+    w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 1000)
+    c, s = _tables(max(qp + Lq, kp + Lk) + 3, max(rot, 16))
+    ref, ref_lse = oracle.sdpa_rope(w["q"], w["k"], w["v"], c.double(), s.double(), rot, style, qp, kp,
+                                    is_causal=causal, scale=np.float32(w["scale"]))
+    q, k, v = (w[n].to(DEV) for n in ("q", "k", "v"))
+    out, lse = sdpa_rope(q, k, v, c.to(DEV), s.to(DEV), rot, style, qp, kp, is_causal=causal,
+                         scale=w["scale"], return_lse=True)
+    assert_close(out, ref, w["q"].dtype, str(case))
+    # The rotated q and k are stored in the input dtype before the attention (as a model
+    # stores them); that rounding (2^-9 relative for bf16, 2^-11 for fp16) moves a score
+    # q'.k' * scale of size ~|q||k|/sqrt(d) ~ sqrt(d) by up to ~sqrt(d) * 2^-8 for bf16,
+    # which the lse carries: bounds 1e-2 (bf16), 3e-3 (fp16), 1e-4 (fp32, no 16-bit copy).
+    tol = {"bf16": 1e-2, "fp16": 3e-3, "fp32": 1e-4}[dt]
+    live = np.isfinite(ref_lse)
+    assert np.abs(to64(lse)[live] - ref_lse[live]).max() < tol
+
+
+def test_rope_arbitrary_tables_and_strided_inputs():
+    # any tables are applied as given (not only rotations), and q/k may be strided views
+    w = random_sdpa_inputs(2, 4, 2, 64, 96, 128, 128, "bf16", seed=11)
+    g = torch.Generator().manual_seed(3)
+    c = torch.randn(200, 64, generator=g)
+    s = torch.randn(200, 64, generator=g)
+    ref, _ = oracle.sdpa_rope(w["q"], w["k"], w["v"], c.double(), s.double(), 128, 0, 7, 100,
+                              scale=np.float32(w["scale"]))
+    q = w["q"].transpose(1, 2).contiguous().to(DEV).transpose(1, 2)    # [B, S, H, D] storage
+    k, v = w["k"].to(DEV), w["v"].to(DEV)
+    out = sdpa_rope(q, k, v, c.to(DEV), s.to(DEV), 128, 0, 7, 100, scale=w["scale"])
+    assert_close(out, ref, torch.bfloat16, "tables + strides")
+
+
+def test_rope_table_and_argument_checks():
+    w = random_sdpa_inputs(1, 2, 2, 10, 10, 64, 64, "bf16", seed=12)
+    q, k, v = (w[n].to(DEV) for n in ("q", "k", "v"))
+    c, s = (t.to(DEV) for t in _tables(12, 64))
+    with pytest.raises(WfError):
+        sdpa_rope(q, k, v, c, s, 64, 0, q_pos0=5)          # positions past the 12 table rows
+    with pytest.raises(WfError):
+        sdpa_rope(q, k, v, c[:, :20], s[:, :20], 40)       # rot_dim not a multiple of 16
+    with pytest.raises(WfError):
+        sdpa_rope(q, k, v, c, s, 64, style=2)
+
+
+def test_rope_full_size_causal_gqa_sampled_rows():
+    # the 4k causal GQA shape (B=4, Hq=32, Hkv=8, d=128) with rotate-half over all 128 dims;
+    # rows [i0, i1) are q rows at positions i0.. against keys 0..i1-1 (bottom-right causal)
+    w = causal_gqa_prefill()
+    c, s = _tables(4096, 128)
+    q, k, v = (w[n].to(DEV) for n in ("q", "k", "v"))
+    out = sdpa_rope(q, k, v, c.to(DEV), s.to(DEV), 128, 0, is_causal=True, scale=w["scale"])
+    G = 4
+    for b, h, i0, i1 in ((0, 0, 0, 64), (1, 13, 1000, 1040), (3, 31, 4032, 4096)):
+        qr = oracle.rope(w["q"][b:b + 1, h:h + 1, i0:i1], c.double(), s.double(), 128, 0, i0)
+        kr = oracle.rope(w["k"][b:b + 1, h // G:h // G + 1, :i1], c.double(), s.double(), 128, 0, 0)
+        ref, _ = oracle.sdpa(qr, kr, w["v"][b:b + 1, h // G:h // G + 1, :i1], is_causal=True,
+                             scale=np.float32(w["scale"]), causal_align="bottom_right")
+        assert_close(out[b:b + 1, h:h + 1, i0:i1], ref, torch.bfloat16, f"b{b} h{h} rows {i0}:{i1}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bshd_hidden_layout_by_strides(causal):
+    # [B, S, H*D] activations (the flattened multi-head layout): heads split out by strides
+    w = random_sdpa_inputs(2, 8, 2, 200, 200, 128, 128, "bf16", seed=13)
+    ref = sdpa(*(w[n].to(DEV) for n in ("q", "k", "v")), is_causal=causal, scale=w["scale"])
+    flat = {n: w[n].transpose(1, 2).reshape(2, 200, -1).contiguous().to(DEV) for n in ("q", "k", "v")}
+    views = {n: flat[n].view(2, 200, -1, 128).transpose(1, 2) for n in flat}   # no copy
+    out = sdpa(views["q"], views["k"], views["v"], is_causal=causal, scale=w["scale"])
+    assert torch.equal(out, ref)
