@@ -4,9 +4,9 @@ The computation lives in libwf.so (hand-written HIP kernels behind the C ABI dec
 include/wf.h); this package only loads it and marshals torch tensors to it.
 """
 from ._lib import ChunkOrderError, CacheConfigError, WfError, load
-from .api import (BlockKVCache, describe, sdpa, sdpa_decode, sdpa_decode_workspace_size,
+from .api import (BlockKVCache, describe, flattened_sdpa, sdpa, sdpa_decode, sdpa_decode_workspace_size,
                   sdpa_rope, varlen_mla_prefill, varlen_mla_prefill_workspace_size)
 
-__all__ = ["sdpa", "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_rope", "varlen_mla_prefill",
+__all__ = ["sdpa", "flattened_sdpa", "sdpa_decode", "sdpa_decode_workspace_size", "sdpa_rope", "varlen_mla_prefill",
            "varlen_mla_prefill_workspace_size", "BlockKVCache", "WfError", "ChunkOrderError",
            "CacheConfigError", "load", "describe"]

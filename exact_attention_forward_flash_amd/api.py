@@ -65,6 +65,27 @@ def sdpa(q, k, v, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,
     return (out, lse) if return_lse else out
 
 
+def flattened_sdpa(q, k, v, num_heads, num_kv_heads=None, attn_mask=None, is_causal=False,
+                   scale=None):
+    """Attention on (batch, sequence, hidden) activations that only lack the head split
+    (WorldFoundry "Core 注意力", section "选择最窄的入口": the flattened multi-head entry):
+    q [B, Sq, Hq*D], k [B, Sk, Hkv*D], v [B, Sk, Hkv*Dv] -> out [B, Sq, Hq*Dv]. The heads are
+    split out by strides and the kernels write the output in place in the flattened layout
+    (no copies); semantics as sdpa()."""
+    kvh = num_heads if num_kv_heads is None else int(num_kv_heads)
+    B, Sq, Sk = q.shape[0], q.shape[1], k.shape[1]
+    qv = q.view(B, Sq, num_heads, -1).transpose(1, 2)
+    kv = k.view(B, Sk, kvh, -1).transpose(1, 2)
+    vv = v.view(B, Sk, kvh, -1).transpose(1, 2)
+    out = torch.empty((B, Sq, num_heads, vv.shape[3]), dtype=q.dtype, device=q.device)
+    lib = _lib.load()
+    dq, dk, dv, dm = describe(qv), describe(kv), describe(vv), describe(attn_mask)
+    do = describe(out.transpose(1, 2))
+    check(lib.wf_sdpa_fwd(_ref(dq), _ref(dk), _ref(dv), _ref(dm), int(bool(is_causal)), 0.0,
+                          _scale(scale), _ref(do), None, _stream(q)))
+    return out.view(B, Sq, -1)
+
+
 def sdpa_rope(q, k, v, cos, sin, rot_dim=None, style=0, q_pos0=0, k_pos0=0, attn_mask=None,
               is_causal=False, scale=None, return_lse=False, workspace=None):
     """sdpa() with rotary position embedding on q and k: cos/sin fp32 [max_pos, rot_dim/2]

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_flash_amd import WfError, sdpa, sdpa_rope
+from exact_attention_forward_flash_amd import WfError, flattened_sdpa, sdpa, sdpa_rope
 from synth import causal_gqa_prefill, random_sdpa_inputs
 from tests.parity import assert_close, to64
 
@@ -103,3 +103,14 @@ def test_bshd_hidden_layout_by_strides(causal):
     views = {n: flat[n].view(2, 200, -1, 128).transpose(1, 2) for n in flat}   # no copy
     out = sdpa(views["q"], views["k"], views["v"], is_causal=causal, scale=w["scale"])
     assert torch.equal(out, ref)
+
+
+def test_flattened_entry_writes_the_flattened_layout():
+    # q [B, S, Hq*D] etc. in, out [B, S, Hq*Dv] written in place: equals sdpa on [B, H, S, D]
+    w = random_sdpa_inputs(2, 8, 4, 100, 140, 64, 64, "fp16", seed=14)
+    ref = sdpa(*(w[n].to(DEV) for n in ("q", "k", "v")), scale=w["scale"])
+    flat = {n: w[n].transpose(1, 2).reshape(2, w[n].shape[2], -1).contiguous().to(DEV)
+            for n in ("q", "k", "v")}
+    out = flattened_sdpa(flat["q"], flat["k"], flat["v"], 8, 4, scale=w["scale"])
+    assert out.shape == (2, 100, 8 * 64)
+    assert torch.equal(out.view(2, 100, 8, 64).transpose(1, 2), ref)
