@@ -776,11 +776,14 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   // slot == token; once it wraps every slot is visible), and a non-causal softmax over keys
   // does not depend on their order, so the kernels read slots [0, n_vis) in place.
   const int dt = kernel_dtype(q->dtype);
-  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, 4, 1, wf::MASK_NONE, 0, wf::MODE_SPLIT);
+  // The query heads of a KV head share each K/V tile (as in wf_sdpa_decode).
+  const int64_t G = Hq / Hkv;
+  const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, 4, hpw, wf::MASK_NONE, 0, wf::MODE_SPLIT);
   if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
   const int n_kt = (int)((n_vis + e->bn - 1) / e->bn);
   const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
-  const int64_t base_blocks = (int64_t)n_qt * B * Hq;
+  const int64_t base_blocks = (int64_t)n_qt * B * Hkv * (G / hpw);
   const int cus = device_cus();
   // About one work group per CU: measured on the 256-query chunk over a 4k window, 192-384
   // groups run 20% faster than 512 (fewer fp32 partials to write and merge).

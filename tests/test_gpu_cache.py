@@ -111,3 +111,27 @@ def test_attend_small_split_and_dense_paths():
             ref, _ = oracle.sdpa(q, kv, vv, scale=np.float32(1.0 / 8.0))
             assert_close(out, ref, torch.bfloat16, f"step {idx}")
             c.after_update(idx)
+
+
+def test_decode_over_the_cache_gqa():
+    """One new query per head over a GQA cache (4 query heads per cached KV head), as in
+    decoding: the attend shares each K/V tile among the query heads of its KV head."""
+    sink, window, chunk = 64, 960, 64
+    shape = (2, 2, sink + window, 128)
+    c = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=torch.float16)
+    o = oracle.BlockKVCacheOracle(shape, shape, 2, chunk, window, sink)
+    g = torch.Generator().manual_seed(21)
+    for idx in range(20):
+        k = torch.randn(2, 2, chunk, 128, generator=g).to(torch.float16)
+        v = torch.randn(2, 2, chunk, 128, generator=g).to(torch.float16)
+        c.before_update(idx)
+        c.update(k.to(DEV), v.to(DEV))
+        o.update(idx, k.float().numpy(), v.float().numpy())
+        if idx in (0, 5, 16, 19):
+            q = torch.randn(2, 8, 1, 128, generator=g).to(torch.float16)
+            kv = torch.from_numpy(o.cached_k()).to(torch.float16)
+            vv = torch.from_numpy(o.cached_v()).to(torch.float16)
+            out = c.attend(q.to(DEV))
+            ref, _ = oracle.sdpa(q, kv, vv, scale=np.float32(1.0 / np.sqrt(128.0)))
+            assert_close(out, ref, torch.float16, f"chunk {idx}")
+        c.after_update(idx)
