@@ -237,6 +237,15 @@ def other_workload(name, steps, warmup):
                     hbm_frac=round(nbytes / (ms * 1e-3) / 8e12, 4),
                     sdpa_fwd_ms=round(ms_dense, 4),
                     sdpa_fwd_gbs=round(nbytes / (ms_dense * 1e-3) / 1e9, 1))
+        # multi-query decode (64 query heads on one KV head): packed (head, position) rows
+        wm = synth.random_sdpa_inputs(B, 64, 1, 1, Lk, D, D, "bf16", seed=8)
+        qm, km, vm = (wm[n].to(dev) for n in ("q", "k", "v"))
+        wsm = torch.empty(max(256, wf.sdpa_decode_workspace_size(qm, km, vm)), dtype=torch.uint8,
+                          device=dev)
+        mbytes = (km.numel() + vm.numel() + 2 * qm.numel()) * 2
+        ms_m = _time_steps(lambda: wf.sdpa_decode(qm, km, vm, workspace=wsm), steps, warmup, stream)
+        line.update(mqa_desc="B=8 Hq=64 Hkv=1, 1 query over 16384 keys", mqa_ms=round(ms_m, 4),
+                    mqa_gbs=round(mbytes / (ms_m * 1e-3) / 1e9, 1))
     else:
         raise SystemExit(f"unknown workload {name}")
     print(json.dumps(line), flush=True)

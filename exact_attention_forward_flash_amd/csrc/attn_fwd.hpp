@@ -36,7 +36,10 @@ namespace wf {
 enum { MASK_NONE = 0, MASK_BOOL = 1, MASK_HALF = 2, MASK_F32 = 3 };
 // MODE_DENSE_P / MODE_DENSE_P16 tag the table rows of the persistent dense kernel
 // (attn_fwd_p.hpp) with fp32 row sums and with row sums over the 16-bit weights.
-enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3, MODE_DENSE_P16 = 4 };
+// MODE_SPLITP: split-KV with the G*Lq (query head, position) rows of a KV head packed into
+// the query rows of the tiles (row r = head r / Lq, position r % Lq), for few queries per head.
+enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3, MODE_DENSE_P16 = 4,
+       MODE_SPLITP = 5 };
 
 struct FwdArgs {
   const void* q; const void* q2; const void* k; const void* k2; const void* v;
@@ -86,6 +89,7 @@ struct AttnFwd {
   static constexpr int BN = 64;
   static constexpr int kNW = NW;
   static constexpr int kHPW = HPW;
+  static constexpr bool kPack = MODE == MODE_SPLITP;  // rows are packed (head, position) pairs
   static constexpr int KCH = DQK / 8;
   static constexpr int VCH = DV / 8;
   static constexpr int WPH = NW / HPW;
@@ -145,6 +149,8 @@ struct AttnFwd {
     const int g = it.hq0 / a.G;
     const float c = a.scale_log2;
 
+    constexpr bool PACK = MODE == MODE_SPLITP;
+    static_assert(!PACK || (HPW == 1 && MASK == MASK_NONE && DQK1 == DQK), "packed rows: plain split only");
     const T* qp = (const T*)a.q + it.b * a.q_sb + hq * a.q_sh + it.qtok0 * a.q_sm;
     const T* q2p = (const T*)a.q2 + it.b * a.q2_sb + hq * a.q2_sh + it.qtok0 * a.q2_sm;
     const T* kp = (const T*)a.k + it.b * a.k_sb + g * a.k_sh + it.ktok0 * a.k_sm;
@@ -155,12 +161,25 @@ struct AttnFwd {
     const int qlo = it.pos0 + qw;
     const int qrow = qlo + j;
     const int qrow_c = qrow < it.Lq ? qrow : it.Lq - 1;
+    // This lane's query: its head, its position (the causal rule) and whether it exists.
+    // Packed rows: row qrow of the item is (head hq0 + qrow / Lq, position qrow % Lq); the
+    // wave's positions then lie anywhere in [0, Lq), so tile ranges use that whole interval.
+    const int prow_c = PACK ? (qrow < a.G * it.Lq ? qrow : a.G * it.Lq - 1) : 0;
+    const int hq_l = PACK ? it.hq0 + prow_c / it.Lq : hq;
+    const int qpos = PACK ? prow_c % it.Lq : qrow;
+    const bool row_ok = PACK ? qrow < a.G * it.Lq : qrow < it.Lq;
+    const int pos_lo = PACK ? 0 : qlo;                 // lowest position of the wave's rows
+    const int pos_hi = PACK ? it.Lq - 1 : qlo + 31;    // highest
     u32x4 qf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int col = 16 * s + 8 * hf;
-      const T* src = (16 * s < DQK1) ? qp + (int64_t)qrow_c * a.q_sm + col
-                                     : q2p + (int64_t)qrow_c * a.q2_sm + (col - DQK1);
+      const T* src;
+      if constexpr (PACK)
+        src = (const T*)a.q + it.b * a.q_sb + hq_l * a.q_sh + (it.qtok0 + qpos) * a.q_sm + col;
+      else
+        src = (16 * s < DQK1) ? qp + (int64_t)qrow_c * a.q_sm + col
+                              : q2p + (int64_t)qrow_c * a.q2_sm + (col - DQK1);
       qf[s] = *reinterpret_cast<const u32x4*>(src);
     }
 
@@ -285,7 +304,7 @@ struct AttnFwd {
     // tile starts past its last query; it still copies tiles and meets the barriers.
     int kt_live = it.kt_hi;
     if (CAUSAL) {
-      const int lim = qlo + 31 + it.shift;
+      const int lim = pos_hi + it.shift;
       const int e = lim < 0 ? 0 : lim / BN + 1;
       kt_live = e < kt_live ? e : kt_live;
     }
@@ -308,7 +327,7 @@ struct AttnFwd {
     // the log2-domain score plus log2(e) m.
     auto need_mask = [&](int kt) {
       const int k0 = kt * BN;
-      return MASK != MASK_NONE || (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > qlo + it.shift);
+      return MASK != MASK_NONE || (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > pos_lo + it.shift);
     };
     // LDS offsets of this lane's mask bytes in a tile (see mswz): 16-bit masks, the 8 bytes
     // of keys 32kb + 8q4 + 4hf .. +3; bool masks, the whole chunks 2kb + q4/2 (q4 even).
@@ -327,7 +346,7 @@ struct AttnFwd {
       const int k0 = kt * BN;
       // Keys past Lk and, for causal calls, keys after the query: only tiles that reach
       // them need the checks.
-      const bool bounds = (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > qlo + it.shift);
+      const bool bounds = (k0 + BN > it.Lk) || (CAUSAL && k0 + BN - 1 > pos_lo + it.shift);
       if constexpr (MASK != MASK_NONE) {
         if (MLDS && a.mask_lds) {
           // This lane's row of the tile (qw + j), keys 32kb + 8q4 + 4hf .. +3, from the LDS
@@ -427,7 +446,7 @@ struct AttnFwd {
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
             bool ok = key < it.Lk;
-            if (CAUSAL) ok = ok && key <= qrow + it.shift;
+            if (CAUSAL) ok = ok && key <= qpos + it.shift;
             sc[kb][r] = ok ? sc[kb][r] : -INFINITY;
           }
       }
@@ -603,9 +622,9 @@ struct AttnFwd {
     const float l = xhalf_sum(l_run);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const float lse2 = l > 0.f ? (m_run == -INFINITY ? 0.f : m_run) + __builtin_log2f(l) : -INFINITY;
-    if (qrow < it.Lq) {
-      if constexpr (MODE == MODE_SPLIT) {
-        const int64_t row = (((int64_t)it.split * a.B + it.b) * a.Hq + hq) * a.Lq + qrow;
+    if (row_ok) {
+      if constexpr (MODE == MODE_SPLIT || MODE == MODE_SPLITP) {
+        const int64_t row = (((int64_t)it.split * a.B + it.b) * a.Hq + hq_l) * a.Lq + qpos;
         float* dst = a.part_o + row * DV;
 #pragma unroll
         for (int n = 0; n < NDV; ++n)
@@ -642,7 +661,8 @@ struct AttnFwd {
 // so their K/V tiles are served from that XCD's L2.
 template <class K, bool CAUSAL>
 __device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int split) {
-  const int GH = a.G / K::kHPW;  // head groups per KV head
+  // head groups per KV head (packed rows: one group holding all G heads)
+  const int GH = K::kPack ? 1 : a.G / K::kHPW;
   const int nbg = a.B * a.Hkv;
   int hsub, bg, t_rank;
   if ((nbg & 7) == 0) {
@@ -673,7 +693,8 @@ __device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int s
   it.qtok0 = 0;
   it.ktok0 = 0;
   it.split = split;
-  const int end = K::tile_end(it.pos0, it.Lk, it.shift);
+  // packed rows hold positions anywhere in [0, Lq): tiles up to the last position's reach
+  const int end = K::tile_end(K::kPack ? it.Lq - K::BMP : it.pos0, it.Lk, it.shift);
   if (split >= 0) {
     it.kt_lo = split * a.tiles_per_split;
     const int hi = it.kt_lo + a.tiles_per_split;
@@ -716,7 +737,7 @@ __device__ __forceinline__ void attn_dispatch(const FwdArgs& a, const RunItem& r
       run_item(it);
       __syncthreads();
     }
-  } else if constexpr (MODE == MODE_SPLIT) {
+  } else if constexpr (MODE == MODE_SPLIT || MODE == MODE_SPLITP) {
     const WorkItem it = decode_grid<K, CAUSAL>(a, blockIdx.x, blockIdx.y);
     run_item(it);
   } else {

@@ -37,6 +37,7 @@ struct AttnFwdP {
   static constexpr int BN = 64;
   static constexpr int kNW = NW;
   static constexpr int kHPW = HPW;
+  static constexpr bool kPack = false;  // rows are packed (head, position) pairs
   static constexpr int KCH = DQK / 8;
   static constexpr int VCH = DV / 8;
   static constexpr int WPH = NW / HPW;

@@ -14,8 +14,16 @@ static const AttnEntry kTable[] = {
     E(128, 1, true),  E(128, 2, true),  E(128, 4, true),
 };
 #undef E
+// packed (query head, position) rows: the G*Lq queries of a KV head share one work item
+#define P(D, CAUSAL) WF_ATTN_ENTRY(__bf16, DT_BF16, D, D, D, 4, 1, MASK_NONE, CAUSAL, MODE_SPLITP)
+static const AttnEntry kTableP[] = {P(64, false), P(64, true), P(128, false), P(128, true)};
+#undef P
 const AttnEntry* attn_table_split_bf16(int* n) {
   *n = (int)(sizeof(kTable) / sizeof(kTable[0]));
   return kTable;
+}
+const AttnEntry* attn_table_splitp_bf16(int* n) {
+  *n = (int)(sizeof(kTableP) / sizeof(kTableP[0]));
+  return kTableP;
 }
 }  // namespace wf

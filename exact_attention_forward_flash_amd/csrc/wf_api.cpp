@@ -113,7 +113,8 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
   static const TableFn tables[] = {wf::attn_table_sdpa_bf16_d64, wf::attn_table_sdpa_bf16_d128,
                                    wf::attn_table_sdpa_f16_d64,  wf::attn_table_sdpa_f16_d128,
                                    wf::attn_table_mla,           wf::attn_table_split_bf16,
-                                   wf::attn_table_split_f16,
+                                   wf::attn_table_split_f16,     wf::attn_table_splitp_bf16,
+                                   wf::attn_table_splitp_f16,
                                    wf::attn_table_w_bf16_d64,    wf::attn_table_w_bf16_d128,
                                    wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128,
                                    wf::attn_table_p_bf16_d64,    wf::attn_table_p_bf16_d128,
@@ -301,18 +302,26 @@ constexpr int64_t kDecodeGroups = 512;
 struct DecodePlan {
   const wf::AttnEntry* e = nullptr;
   int n_qt = 0, n_splits = 1, tps = 1;
+  bool pack = false;   // (query head, position) rows packed: one item per KV head and row block
+  int64_t base = 0;    // work items before the split
 };
 DecodePlan decode_plan(int dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, int64_t Lk,
                        int64_t D, int64_t Dv, bool causal) {
   DecodePlan p;
   if (Hkv <= 0 || Hq % Hkv != 0) return p;
   const int64_t G = Hq / Hkv;
-  const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  // More than 4 query heads per KV head: pack the G*Lq (head, position) rows of a KV head into
+  // the tiles' query rows, so each K/V tile is read once per KV head (not once per 4 heads).
+  p.pack = G > 4 && G * Lq <= 0x7fffffff;
+  if (const char* t = getenv("WF_TUNE_DECODE_PACK")) p.pack = p.pack && atoi(t) != 0;
+  const int hpw = p.pack ? 1 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
   p.e = find_attn(dt, (int)D, (int)D, (int)Dv, 4, hpw, wf::MASK_NONE, causal ? 1 : 0,
-                  wf::MODE_SPLIT);
+                  p.pack ? wf::MODE_SPLITP : wf::MODE_SPLIT);
   if (p.e == nullptr) return p;
-  p.n_qt = (int)((Lq + p.e->bmp - 1) / p.e->bmp);
-  const int64_t base = std::max<int64_t>(1, (int64_t)p.n_qt * B * Hkv * (G / hpw));
+  const int64_t rows = p.pack ? G * Lq : Lq;
+  p.n_qt = (int)((rows + p.e->bmp - 1) / p.e->bmp);
+  p.base = (int64_t)p.n_qt * B * Hkv * (p.pack ? 1 : G / hpw);
+  const int64_t base = std::max<int64_t>(1, p.base);
   const int64_t n_kt = (Lk + p.e->bn - 1) / p.e->bn;
   int64_t groups = kDecodeGroups, min_tiles = 2;
   if (const char* t = getenv("WF_TUNE_DECODE_GROUPS")) groups = std::max(1, atoi(t));
@@ -871,7 +880,7 @@ int wf_sdpa_decode(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, i
     return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (rows == 0 || Dv == 0) return ok();
   const int64_t G = Hq / Hkv;
-  const int64_t base_blocks = (int64_t)p.n_qt * B * Hkv * (G / p.e->hpw);
+  const int64_t base_blocks = p.base;
   if (base_blocks > 0x7fffffff) return fail(WF_ERR_SHAPE, "problem too large for one launch");
   wf::FwdArgs a;
   std::memset(&a, 0, sizeof(a));

@@ -28,6 +28,8 @@ const AttnEntry* attn_table_sdpa_f16_d128(int* n);
 const AttnEntry* attn_table_mla(int* n);
 const AttnEntry* attn_table_split_bf16(int* n);
 const AttnEntry* attn_table_split_f16(int* n);
+const AttnEntry* attn_table_splitp_bf16(int* n);
+const AttnEntry* attn_table_splitp_f16(int* n);
 const AttnEntry* attn_table_w_bf16_d128(int* n);
 const AttnEntry* attn_table_w_bf16_d64(int* n);
 const AttnEntry* attn_table_w_f16_d128(int* n);

@@ -23,6 +23,10 @@ CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, causal
     ("bf16", 1, 16, 16, 33, 2048, 128, True),   # two query tiles
     ("fp16", 2, 12, 4, 2, 777, 64, False),      # GQA 3 (one head per work group)
     ("bf16", 1, 64, 8, 1, 130, 128, False),     # GQA 8, few tiles: one split
+    # more than 4 heads per KV head: (head, position) rows packed into the tiles
+    ("bf16", 1, 64, 1, 1, 8192, 128, False),    # multi-query: 64 heads on one KV head
+    ("fp16", 2, 16, 2, 3, 2000, 64, True),      # GQA 8, 3 new tokens each, causal
+    ("bf16", 1, 48, 1, 5, 700, 128, True),      # 240 packed rows: two row blocks
 ]
 
 
@@ -82,3 +86,12 @@ def test_decode_bench_shape_sampled():
         ref, _ = oracle.sdpa(w["q"][b:b + 1], w["k"][b:b + 1], w["v"][b:b + 1],
                              scale=np.float32(w["scale"]))
         assert_close(out[b:b + 1], ref, torch.bfloat16, f"batch {b}")
+
+
+def test_packed_rows_match_unpacked(monkeypatch):
+    # the same call with (head, position) packing turned off agrees within rounding
+    w = random_sdpa_inputs(2, 32, 2, 2, 3000, 128, 128, "bf16", seed=8)
+    packed = _run(w, True)
+    monkeypatch.setenv("WF_TUNE_DECODE_PACK", "0")
+    plain = _run(w, True)
+    assert (packed.float() - plain.float()).abs().max().item() < 2e-2
