@@ -60,6 +60,7 @@ struct FwdArgs {
   // varlen (persistent) mode
   const int* cu_q; const int* cu_k; const int2* items; int* counter; const int* n_items;
   int kv_padded;      // K/V rows of sequence i start at i * k_sb (padded), not at cu_k[i]
+  int xcd_parts;      // work split over the 8 XCDs by KV head (counter[16 + 4x] for XCD x)
   // split-KV mode
   int tiles_per_split; float* part_o; float* part_lse;
 };
@@ -714,16 +715,26 @@ __device__ __forceinline__ void attn_dispatch(const FwdArgs& a, const RunItem& r
   if constexpr (MODE == MODE_VARLEN) {
     __shared__ int s_item;
     const int NHG = a.Hq / K::kHPW;        // head groups per (sequence, query tile) item
-    const int n_work = *a.n_items * NHG;
+    // With xcd_parts, work group p (on XCD p % 8: the hardware deals work groups to the XCDs
+    // round-robin) takes only the head groups of KV heads g = p % 8 (mod 8), from that XCD's
+    // own counter over the same longest-first list: a sequence's K/V for one KV head is then
+    // read into one XCD's L2 instead of into all eight.
+    const int part = a.xcd_parts ? (int)(blockIdx.x & 7) : 0;
+    int* const ctr = a.xcd_parts ? a.counter + 16 + 4 * part : a.counter;
+    const int per_kv = a.G / K::kHPW;      // head groups per KV head
+    const int nhg = a.xcd_parts ? NHG / 8 : NHG;
+    const int n_work = *a.n_items * nhg;
     for (;;) {
-      if (threadIdx.x == 0) s_item = atomicAdd(a.counter, 1);
+      if (threadIdx.x == 0) s_item = atomicAdd(ctr, 1);
       __syncthreads();
       const int idx = s_item;
       if (idx >= n_work) break;
-      const int2 pr = a.items[idx / NHG];
+      const int2 pr = a.items[idx / nhg];
+      int hg = idx % nhg;
+      if (a.xcd_parts) hg = (part + 8 * (hg / per_kv)) * per_kv + hg % per_kv;
       WorkItem it;
       it.b = pr.x;
-      it.hq0 = (idx % NHG) * K::kHPW;
+      it.hq0 = hg * K::kHPW;
       it.pos0 = pr.y * K::BMP;
       const int cq0 = a.cu_q[it.b], ck0 = a.cu_k[it.b];
       it.Lq = a.cu_q[it.b + 1] - cq0;

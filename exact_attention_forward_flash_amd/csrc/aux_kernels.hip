@@ -133,6 +133,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
       }
     }
   }
+  if (t < 8) ws[16 + 4 * t] = 0;   // per-XCD work counters
   if (t == 0) {
     ws[0] = 0;        // work counter
     ws[1] = n_pairs;  // number of (sequence, tile) items; heads are expanded by the kernel

@@ -647,7 +647,12 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
   // needs an upper bound on the work.
   const int64_t total_work = (int64_t)max_items * (head_num / e->hpw);
   const int cus = device_cus();
-  const int grid = (int)(total_work < cus ? total_work : cus);
+  int grid = (int)(total_work < cus ? total_work : cus);
+  // Split the work over the 8 XCDs by KV head when the heads and the grid divide evenly (the
+  // head groups of one KV head never straddle XCDs); WF_TUNE_MLA_XCD=0 turns it off.
+  a.xcd_parts = kv_head_num % 8 == 0 && (head_num / kv_head_num) % e->hpw == 0 && cus % 8 == 0;
+  if (const char* t = getenv("WF_TUNE_MLA_XCD")) a.xcd_parts = a.xcd_parts && atoi(t) != 0;
+  if (a.xcd_parts) grid = (grid + 7) / 8 * 8;
   return hip_status(launch(e->fn, dim3(grid), dim3(e->nw * 64), a, s), "MLA launch");
 }
 

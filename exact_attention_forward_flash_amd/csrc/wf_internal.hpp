@@ -98,7 +98,8 @@ hipError_t launch_kv_gather(int unit, int esize, const void* cache, const int64_
 
 // Varlen workspace layout (bytes from the workspace base).
 struct VarlenWs {
-  static constexpr int64_t kHeaderInts = 64;  // [0] counter, [1] n_items, [2] error
+  // [0] counter, [1] n_items, [2] error, [16 + 4x] the work counter of XCD x (x < 8)
+  static constexpr int64_t kHeaderInts = 64;
   __host__ __device__ static int64_t cu_q_off() { return kHeaderInts * 4; }
   __host__ __device__ static int64_t cu_k_off(int batch) { return cu_q_off() + align(((int64_t)batch + 1) * 4); }
   __host__ __device__ static int64_t items_off(int batch) { return cu_k_off(batch) + align(((int64_t)batch + 1) * 4); }
