@@ -421,10 +421,13 @@ int sdpa_validate(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
       mask_vec = reinterpret_cast<uintptr_t>(mask->data) % (4 * ms) == 0;
       for (int i = 0; i < 3; ++i)
         if (mask->shape[i] > 1 && mask->stride[i] % 4 != 0) mask_vec = false;
-      // Bool / 16-bit mask tiles can be copied into LDS when every row starts 16-byte aligned
-      // and 256 rows span less than 2 GiB (32-bit per-lane copy offsets).
+      // Bool / 16-bit mask tiles can be copied into LDS when every row starts 16-byte aligned,
+      // 256 rows span less than 2 GiB (32-bit per-lane copy offsets) and a row's keys end on a
+      // dword boundary: the copy's bounds check zeroes whole dwords, so a last row ending
+      // inside a dword would lose its last valid keys (those masks read global memory).
       mask_lds = mask_kind != wf::MASK_F32 && reinterpret_cast<uintptr_t>(mask->data) % 16 == 0 &&
-                 mask->stride[2] >= 0 && mask->stride[2] * ms * 256 < ((int64_t)1 << 31);
+                 mask->stride[2] >= 0 && mask->stride[2] * ms * 256 < ((int64_t)1 << 31) &&
+                 (Lk * ms) % 4 == 0;
       for (int i = 0; i < 3; ++i)
         if (mask->shape[i] > 1 && (mask->stride[i] * ms) % 16 != 0) mask_lds = false;
     }

@@ -233,3 +233,21 @@ def test_masked_sdpa_full_size(kind):
     out = run(w)
     ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w["mask"], scale=np.float32(w["scale"]))
     assert_close(out, ref, torch.float16, f"masked {kind}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp16"])
+def test_mask_rows_ending_inside_a_dword(dt):
+    # Masks whose rows are 16-byte aligned (one query row, or padded rows viewed narrower)
+    # but whose key count is not a multiple of 4 bytes: the last valid keys must count.
+    g = torch.Generator().manual_seed(5)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dt]
+    for Lq, Lk in ((1, 255), (70, 253)):
+        q = torch.randn(1, 8, Lq, 64, generator=g).to(tdt)
+        k = torch.randn(1, 4, Lk, 64, generator=g).to(tdt)
+        v = torch.randn(1, 4, Lk, 64, generator=g).to(tdt)
+        wide = torch.rand(1, 1, Lq, 256, generator=g) < 0.85        # rows 256 bytes apart
+        m = wide[..., :Lk]
+        ref, _ = oracle.sdpa(q, k, v, mask=m.contiguous(), scale=np.float32(0.125))
+        out = sdpa(q.to(DEV), k.to(DEV), v.to(DEV), attn_mask=m.to(DEV) if Lq == 1 else
+                   wide.to(DEV)[..., :Lk], scale=0.125)
+        assert_close(out, ref, tdt, f"Lq={Lq} Lk={Lk}")
