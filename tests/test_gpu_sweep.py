@@ -8,12 +8,12 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_flash_amd import sdpa
+from exact_attention_forward_flash_amd import sdpa, sdpa_decode, sdpa_rope, varlen_mla_prefill
 from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-N_CASES = 40
+N_CASES = 100
 
 
 def _case(i):
@@ -69,3 +69,99 @@ def test_random_case(i):
     else:
         out = sdpa(*args, attn_mask=md, is_causal=c["causal"], scale=scale)
     assert_close(out, ref, dt, str(c))
+
+
+
+# ---------------------------------------------------------------- decode --------------------
+
+@pytest.mark.parametrize("i", range(30))
+def test_random_decode(i):
+    r = np.random.default_rng(5000 + i)
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[str(r.choice(["bf16", "fp16"]))]
+    B, Hkv = int(r.integers(1, 4)), int(r.choice([1, 2, 4, 8]))
+    G = int(r.choice([1, 2, 3, 4, 6, 8, 16]))
+    D = int(r.choice([64, 128]))
+    Lq = int(r.choice([1, 1, 2, 3, 5, 8]))
+    Lk = int(r.choice([0, 1, 63, 64, 65, 500, 1999, 4096]))
+    causal = bool(r.random() < 0.5)
+    g = torch.Generator().manual_seed(i)
+    q = torch.randn(B, Hkv * G, Lq, D, generator=g).to(dt)
+    k = torch.randn(B, Hkv, Lk, D, generator=g).to(dt)
+    v = torch.randn(B, Hkv, Lk, D, generator=g).to(dt)
+    ref, ref_lse = oracle.sdpa(q, k, v, is_causal=causal, scale=np.float32(1 / np.sqrt(D)),
+                               causal_align="bottom_right")
+    out, lse = sdpa_decode(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=causal,
+                           scale=1 / np.sqrt(D), return_lse=True)
+    what = f"decode case {i}: B={B} Hkv={Hkv} G={G} D={D} Lq={Lq} Lk={Lk} causal={causal}"
+    assert_close(out, ref, dt, what)
+    live = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(to64(lse)), live), what
+    if live.any():
+        assert np.abs(to64(lse)[live] - ref_lse[live]).max() < 1e-3, what
+
+
+# ---------------------------------------------------------------- MLA prefill ---------------
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_mla(i):
+    r = np.random.default_rng(7000 + i)
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[str(r.choice(["bf16", "fp16"]))]
+    batch = int(r.integers(1, 6))
+    H = int(r.choice([1, 2, 4, 8, 16]))
+    Hkv = int(r.choice([h for h in (1, 2, 4, 8, 16) if H % h == 0]))
+    qlens = [int(x) for x in r.choice([0, 1, 2, 63, 64, 65, 255, 256, 257, 700], batch)]
+    kvlens = [q if r.random() < 0.5 else int(r.choice([0, 1, 70, 300, 800])) for q in qlens]
+    mt = int(r.integers(0, 2))
+    padded = bool(r.random() < 0.3)
+    g = torch.Generator().manual_seed(100 + i)
+    nq, nk = sum(qlens), sum(kvlens)
+    q, qr = torch.randn(nq, H, 128, generator=g).to(dt), torch.randn(nq, H, 64, generator=g).to(dt)
+    k, kr = torch.randn(nk, Hkv, 128, generator=g).to(dt), torch.randn(nk, Hkv, 64, generator=g).to(dt)
+    v = torch.randn(nk, Hkv, 128, generator=g).to(dt)
+    ql, kl = torch.tensor(qlens, dtype=torch.int32), torch.tensor(kvlens, dtype=torch.int32)
+    scale = 1 / np.sqrt(192.0)
+    ref = oracle.varlen_mla_prefill(q, qr, k, kr, v, ql, kl, H, Hkv, np.float32(scale), mt)
+    if padded:   # the same tokens, [batch, max_seq, Hkv, d] with zero padding rows
+        ms = max(max(kvlens), 1)
+        cu = np.concatenate([[0], np.cumsum(kvlens)])
+        pads = []
+        for t in (k, kr, v):
+            p = torch.zeros((batch, ms) + tuple(t.shape[1:]), dtype=dt)
+            for b in range(batch):
+                p[b, :kvlens[b]] = t[cu[b]:cu[b + 1]]
+            pads.append(p.to(DEV))
+        kd, krd, vd = pads
+    else:
+        kd, krd, vd = k.to(DEV), kr.to(DEV), v.to(DEV)
+    out = varlen_mla_prefill(q.to(DEV), qr.to(DEV), kd, krd, vd, ql.to(DEV), kl.to(DEV), H, Hkv,
+                             scale, mt, kv_layout="padded" if padded else "packed")
+    assert_close(out, ref, dt, f"MLA case {i}: q {qlens} kv {kvlens} H={H}/{Hkv} mask={mt} padded={padded}")
+
+
+# ---------------------------------------------------------------- RoPE ----------------------
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_rope(i):
+    r = np.random.default_rng(9000 + i)
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[str(r.choice(["bf16", "fp16"]))]
+    B, Hkv, G = int(r.integers(1, 3)), int(r.choice([1, 2, 4])), int(r.choice([1, 2, 4]))
+    D = int(r.choice([64, 128]))
+    rot = int(r.choice([d for d in (16, 32, 48, 64, 96, 128) if d <= D]))
+    style = int(r.integers(0, 2))
+    Lq, Lk = int(r.choice([1, 33, 128, 300])), int(r.choice([1, 64, 200, 400]))
+    qp, kp = int(r.integers(0, 50)), int(r.integers(0, 50))
+    causal = bool(r.random() < 0.4)
+    g = torch.Generator().manual_seed(300 + i)
+    q = torch.randn(B, Hkv * G, Lq, D, generator=g).to(dt)
+    k = torch.randn(B, Hkv, Lk, D, generator=g).to(dt)
+    v = torch.randn(B, Hkv, Lk, D, generator=g).to(dt)
+    npos = max(qp + Lq, kp + Lk)
+    theta = 10000.0 ** (-np.arange(rot // 2) * 2.0 / rot)
+    ang = np.arange(npos)[:, None] * theta[None, :]
+    c, s_ = torch.from_numpy(np.cos(ang)).float(), torch.from_numpy(np.sin(ang)).float()
+    ref, _ = oracle.sdpa_rope(q, k, v, c.double(), s_.double(), rot, style, qp, kp,
+                              is_causal=causal, scale=np.float32(1 / np.sqrt(D)))
+    out = sdpa_rope(q.to(DEV), k.to(DEV), v.to(DEV), c.to(DEV), s_.to(DEV), rot, style, qp, kp,
+                    is_causal=causal, scale=1 / np.sqrt(D))
+    assert_close(out, ref, dt, f"rope case {i}: B={B} Hkv={Hkv} G={G} D={D} rot={rot} style={style} "
+                               f"Lq={Lq} Lk={Lk} pos={qp},{kp} causal={causal}")
