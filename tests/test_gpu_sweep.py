@@ -165,3 +165,38 @@ def test_random_rope(i):
                     is_causal=causal, scale=1 / np.sqrt(D))
     assert_close(out, ref, dt, f"rope case {i}: B={B} Hkv={Hkv} G={G} D={D} rot={rot} style={style} "
                                f"Lq={Lq} Lk={Lk} pos={qp},{kp} causal={causal}")
+
+
+# ---------------------------------------------------------------- block KV cache attend -----
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_cache_attend(i):
+    from exact_attention_forward_flash_amd import BlockKVCache
+    r = np.random.default_rng(11000 + i)
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[str(r.choice(["bf16", "fp16"]))]
+    chunk = int(r.choice([16, 64, 128]))
+    window = chunk * int(r.integers(1, 6))
+    sink = chunk * int(r.integers(0, 3))
+    Hkv, G, D = int(r.choice([1, 2, 4])), int(r.choice([1, 2, 4, 8])), int(r.choice([64, 128]))
+    B = int(r.integers(1, 3))
+    shape = (B, Hkv, sink + window, D)
+    c = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=dt)
+    o = oracle.BlockKVCacheOracle(shape, shape, 2, chunk, window, sink)
+    g = torch.Generator().manual_seed(400 + i)
+    steps = int(r.integers(1, 14))
+    for idx in range(steps):
+        k = torch.randn(B, Hkv, chunk, D, generator=g).to(dt)
+        v = torch.randn(B, Hkv, chunk, D, generator=g).to(dt)
+        c.before_update(idx)
+        c.update(k.to(DEV), v.to(DEV))
+        o.update(idx, k.float().numpy(), v.float().numpy())
+        c.after_update(idx)
+    Lq = int(r.choice([1, 3, chunk]))
+    q = torch.randn(B, Hkv * G, Lq, D, generator=g).to(dt)
+    kv = torch.from_numpy(o.cached_k()).to(dt)
+    vv = torch.from_numpy(o.cached_v()).to(dt)
+    assert torch.equal(c.cached_k().cpu(), kv)
+    ref, _ = oracle.sdpa(q, kv, vv, scale=np.float32(1 / np.sqrt(D)))
+    out = c.attend(q.to(DEV))
+    assert_close(out, ref, dt, f"cache case {i}: sink={sink} window={window} chunk={chunk} "
+                               f"B={B} Hkv={Hkv} G={G} D={D} steps={steps} Lq={Lq}")
