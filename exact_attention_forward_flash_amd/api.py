@@ -212,6 +212,12 @@ class BlockKVCache:
             raise RuntimeError("after_update() index differs from before_update()")
         self._pending = None
 
+    def n_visible(self):
+        """Number of visible cached tokens (the library's count, without the slot list)."""
+        n = ctypes.c_int64()
+        check(_lib.load().wf_block_kv_visible(ctypes.byref(self.state), ctypes.byref(n), None))
+        return n.value
+
     def visible(self):
         """(n_visible, slot of each visible token in chronological order) from the library."""
         lib = _lib.load()

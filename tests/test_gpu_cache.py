@@ -82,8 +82,8 @@ def test_cache_stream(heads, check_chunks):
         c.update(k.to(DEV), v.to(DEV))
         o.update(idx, k.numpy(), v.numpy())
         if idx in check_chunks:
-            n, _ = c.visible()
-            assert n == min((idx + 1) * 256, 4096)
+            n, slots = c.visible()
+            assert n == min((idx + 1) * 256, 4096) == c.n_visible() == len(slots)
             assert np.array_equal(c.cached_k().cpu().numpy(), o.cached_k())
             _attend_check(c, o, q, f"chunk {idx}")
         else:
