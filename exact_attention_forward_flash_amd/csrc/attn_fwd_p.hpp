@@ -21,6 +21,9 @@
 // KV group on one XCD) in rounds over the XCD's P/8 groups, alternating direction each round,
 // which pairs long and short causal items on every CU.
 //
+// ROPE instantiations turn Q by a rotate-half rotary table over the whole head as it is read
+// into registers (once per item), so that such calls need a separate pass over K only.
+//
 // Every wave of a group must compute the same tiles, so for causal calls the group covers
 // one 64-key tile's worth of positions (BMP == BN, HPW = 4 with 8 waves) and the causal
 // alignment shift is 0; the host routes other calls to the one-item-per-group kernels.
@@ -31,7 +34,7 @@ namespace wf {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16>
+template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16, bool ROPE = false>
 struct AttnFwdP {
   static constexpr int NW = 8;
   static constexpr int BN = 64;
@@ -188,17 +191,54 @@ struct AttnFwdP {
     // 1e-4, which moves the log-sum-exp by a few 1e-4 (measured on N(0,1) inputs: output
     // error up to ~1e-3, as large as the output's own rounding). Calls that ask for the lse
     // therefore keep Q as it is and scale every score in fp32.
+    //
+    // ROPE: Q is turned first (rotate-half over all DQK dims), in fp32, and rounded once. Both
+    // members of every pair sit in the lane's own registers (chunk s pairs with chunk
+    // s + NS/2). The table rows are read from global memory (they stay in L2: one row per
+    // query position, shared by every head and batch).
     u32x4 qf[NS];
-    auto read_q = [&]() {
+    auto read_q = [&](const Item& it) {
       typedef typename Mfma16<T>::v8 v8;
+      auto chunk = [&](int s) {
+        return __builtin_bit_cast(v8, lds_read16(sQw + j * KCH * 16 + (((2 * s + hf) ^ kswz(j)) * 16)));
+      };
+      auto put = [&](int s, const float* y) {
+        v8 r;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const u32x4 raw = lds_read16(sQw + j * KCH * 16 + (((2 * s + hf) ^ kswz(j)) * 16));
-        const v8 x = __builtin_bit_cast(v8, raw);
-        v8 y;
+        for (int e = 0; e < 8; ++e) r[e] = (T)(PRESCALE ? y[e] * c : y[e]);
+        qf[s] = __builtin_bit_cast(u32x4, r);
+      };
+      if constexpr (!ROPE) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = PRESCALE ? (T)((float)x[e] * c) : x[e];
-        qf[s] = __builtin_bit_cast(u32x4, y);
+        for (int s = 0; s < NS; ++s) {
+          const v8 x = chunk(s);
+          v8 y;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = PRESCALE ? (T)((float)x[e] * c) : x[e];
+          qf[s] = __builtin_bit_cast(u32x4, y);
+        }
+      } else {   // rotate-half over all DQK dims: chunk s pairs with chunk s + NS/2
+        int p = it.pos0 + qw + j;
+        p = p < a.Lq ? p : a.Lq - 1;   // rows past Lq are not stored; keep their reads in the table
+        const float* cr = a.rq_cos + (int64_t)p * (DQK / 2);
+        const float* sr = a.rq_sin + (int64_t)p * (DQK / 2);
+#pragma unroll
+        for (int s = 0; s < NS / 2; ++s) {
+          const int i0 = 16 * s + 8 * hf;
+          const f32x4 c0 = *(const f32x4*)(cr + i0), c1 = *(const f32x4*)(cr + i0 + 4);
+          const f32x4 n0 = *(const f32x4*)(sr + i0), n1 = *(const f32x4*)(sr + i0 + 4);
+          const v8 xa = chunk(s), xb = chunk(s + NS / 2);
+          float ya[8], yb[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float cv = e < 4 ? c0[e] : c1[e - 4], sv = e < 4 ? n0[e] : n1[e - 4];
+            const float fa = (float)xa[e], fb = (float)xb[e];
+            ya[e] = fmaf(fa, cv, -fb * sv);
+            yb[e] = fmaf(fb, cv, fa * sv);
+          }
+          put(s, ya);
+          put(s + NS / 2, yb);
+        }
       }
     };
 
@@ -492,7 +532,7 @@ struct AttnFwdP {
     advance(ck, false);
     wait_vmem();
     __syncthreads();
-    read_q();
+    read_q(cur_it);
     s_tile(sK0, sc);
     if (need_mask(0, cur_it.pos0)) apply_mask(0, cur_it.pos0, sc);
     mt_cur = tile_max(sc);
@@ -512,7 +552,7 @@ struct AttnFwdP {
                     WF_LDS char* Vfill, f32x16* cur, f32x16* nxt) {
       const bool last = u + 1 == cur_it.n;
       if (last) {
-        read_q();
+        read_q(nxt_it);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         stage_q(item_at(list, cur_it.k + 2));
       }
@@ -552,10 +592,10 @@ struct AttnFwdP {
   }
 };
 
-template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16>
+template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16, bool ROPE = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_p_kernel(FwdArgs a) {
-  typedef AttnFwdP<T, DQK, DV, HPW, CAUSAL, SUM16> K;
+  typedef AttnFwdP<T, DQK, DV, HPW, CAUSAL, SUM16, ROPE> K;
   // Separate LDS arrays, so that the compiler can tell a tile copy into one buffer from the
   // operand reads of another and does not wait for the copy before them. The tile buffers
   // carry the largest alignment, which places them first: every operand read in the tile loop

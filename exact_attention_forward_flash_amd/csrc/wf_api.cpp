@@ -118,7 +118,8 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
                                    wf::attn_table_w_bf16_d64,    wf::attn_table_w_bf16_d128,
                                    wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128,
                                    wf::attn_table_p_bf16_d64,    wf::attn_table_p_bf16_d128,
-                                   wf::attn_table_p_f16_d64,     wf::attn_table_p_f16_d128};
+                                   wf::attn_table_p_f16_d64,     wf::attn_table_p_f16_d128,
+                                   wf::attn_table_p_rope_bf16,   wf::attn_table_p_rope_f16};
   for (TableFn f : tables) {
     int n = 0;
     const wf::AttnEntry* t = f(&n);
@@ -186,11 +187,50 @@ int resolve_scale(float scale, int64_t dqk, float* out) {
   return WF_OK;
 }
 
+// Persistent form of the 32-query kernel (one work group per CU walking a list of work
+// items): calls without a mask whose Q/K/V copy offsets fit in 32 bits and, when causal, whose
+// work groups cover one 64-key tile of query positions (HPW = 4). Returns the table entry and
+// sets the query-tile count and the grid, or returns nullptr when the call takes the
+// one-item-per-group kernels. rope: the variant that turns Q by a rotary table.
+// WF_TUNE_PERSIST=0 turns it off.
+static const wf::AttnEntry* persist_plan(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
+                                         int mask_kind, int causal, bool has_lse, int64_t Lk,
+                                         bool rope, int* n_qtiles, int64_t* grid) {
+  const int dt = kernel_dtype(q->dtype);
+  if (dt == wf::DT_F32 || mask_kind != wf::MASK_NONE || Lk <= 0) return nullptr;
+  const int B = (int)q->shape[0], Hq = (int)q->shape[1], Lq = (int)q->shape[2];
+  const int Dqk = (int)q->shape[3], Hkv = (int)k->shape[1], Dv = (int)v->shape[3];
+  const int G = Hq / Hkv;
+  int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  if (const char* t = getenv("WF_TUNE_HPW")) { int h = atoi(t); if (h >= 1 && h <= hpw && G % h == 0) hpw = h; }
+  const int64_t max_sm = std::max(k->stride[2], v->stride[2]);
+  const bool kv_ok = max_sm >= 0 && max_sm * 2 * 64 < ((int64_t)1 << 31);
+  const bool q_ok = q->stride[2] >= 0 && q->stride[2] * 2 * 32 < ((int64_t)1 << 31);
+  bool persist = kv_ok && q_ok && (!causal || hpw == 4);
+  if (const char* t = getenv("WF_TUNE_PERSIST")) persist = persist && atoi(t) != 0;
+  if (!persist) return nullptr;
+  // Without the lse the row sums are taken over the 16-bit weights (exactly the weights
+  // that multiply V; their sum keeps the 16-bit rounding, which the lse would show).
+  const int pmode = rope ? (has_lse ? wf::MODE_DENSE_PR : wf::MODE_DENSE_PR16)
+                         : (has_lse ? wf::MODE_DENSE_P : wf::MODE_DENSE_P16);
+  const wf::AttnEntry* pe = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, wf::MASK_NONE, causal, pmode);
+  const int ncu = cu_count();
+  if (pe == nullptr || ncu <= 0) return nullptr;
+  *n_qtiles = (Lq + pe->bmp - 1) / pe->bmp;
+  const int64_t items = (int64_t)*n_qtiles * B * Hkv * (G / hpw);
+  const int64_t P = std::min<int64_t>(ncu, items);
+  if (P <= 0 || (items + P - 1) / P > wf::kPersistMaxItems) return nullptr;
+  *grid = P;
+  return pe;
+}
+
 // Dense attention over already validated operands (shared by SDPA and the cache attend when
-// a single split suffices). mask_kind: wf::MASK_*.
+// a single split suffices). mask_kind: wf::MASK_*. rope_q: turn Q by this rotate-half table
+// over the whole head on its way into the persistent kernel (the caller has checked with
+// persist_plan that the call takes it).
 int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const wf_tensor* mask,
               int mask_kind, bool mask_vec, bool mask_lds, int causal, float scale, wf_tensor* out, float* lse,
-              int64_t Lk, hipStream_t stream) {
+              int64_t Lk, hipStream_t stream, const wf_rope* rope_q = nullptr) {
   const int B = (int)q->shape[0], Hq = (int)q->shape[1], Lq = (int)q->shape[2];
   const int Dqk = (int)q->shape[3], Hkv = (int)k->shape[1], Dv = (int)v->shape[3];
   const int G = Hq / Hkv;
@@ -230,26 +270,21 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   // 64 rows of K and of V must span less than 2 GiB. WF_TUNE_QPW=32|64 overrides.
   const int64_t max_sm = std::max(k->stride[2], v->stride[2]);
   const bool w64_ok = max_sm >= 0 && max_sm * 2 * 64 < ((int64_t)1 << 31);
-  // Persistent form of the 32-query kernel (one work group per CU walking a list of work
-  // items): calls without a mask whose Q/K/V copy offsets fit in 32 bits and, when causal,
-  // whose work groups cover one 64-key tile of query positions (HPW = 4). WF_TUNE_PERSIST=0
-  // turns it off.
-  const bool q_ok = q->stride[2] >= 0 && q->stride[2] * 2 * 32 < ((int64_t)1 << 31);
-  bool persist = mask_kind == wf::MASK_NONE && Lk > 0 && w64_ok && q_ok && (!causal || hpw == 4);
-  if (const char* t = getenv("WF_TUNE_PERSIST")) persist = persist && atoi(t) != 0;
-  if (persist) {
-    // Without the lse the row sums are taken over the 16-bit weights (exactly the weights
-    // that multiply V; their sum keeps the 16-bit rounding, which the lse would show).
-    const int pmode = lse == nullptr ? wf::MODE_DENSE_P16 : wf::MODE_DENSE_P;
-    const wf::AttnEntry* pe = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, wf::MASK_NONE, causal, pmode);
-    const int ncu = cu_count();
-    if (pe != nullptr && ncu > 0) {
-      a.n_qtiles = (Lq + pe->bmp - 1) / pe->bmp;
-      const int64_t items = (int64_t)a.n_qtiles * B * Hkv * (G / hpw);
-      const int64_t P = std::min<int64_t>(ncu, items);
-      if (P > 0 && (items + P - 1) / P <= wf::kPersistMaxItems)
-        return hip_status(launch(pe->fn, dim3((unsigned)P), dim3(512), a, stream), "attention launch");
+  {
+    int nqt = 0;
+    int64_t P = 0;
+    const wf::AttnEntry* pe = persist_plan(q, k, v, mask_kind, causal, lse != nullptr, Lk,
+                                           rope_q != nullptr, &nqt, &P);
+    if (pe != nullptr) {
+      a.n_qtiles = nqt;
+      if (rope_q != nullptr) {
+        const int64_t row0 = rope_q->q_pos0 * (rope_q->rot_dim / 2);
+        a.rq_cos = rope_q->cos + row0;
+        a.rq_sin = rope_q->sin + row0;
+      }
+      return hip_status(launch(pe->fn, dim3((unsigned)P), dim3(512), a, stream), "attention launch");
     }
+    if (rope_q != nullptr) return fail(WF_ERR_UNSUPPORTED, "rotary Q needs the persistent kernel");
   }
   // Masked calls take the 32-query kernel, which copies bool / 16-bit mask tiles into LDS.
   int qpw = (lse == nullptr && !causal && w64_ok && !(mask_lds && mask_kind != wf::MASK_NONE)) ? 64 : 32;
@@ -513,10 +548,21 @@ int wf_sdpa_rope_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
     return d;
   };
   hipStream_t strm = (hipStream_t)stream;
-  hipError_t he = wf::launch_rope(kernel_dtype(q->dtype), desc(q, &qr, rope->q_pos0),
-                                  desc(k, &kr, rope->k_pos0), (int)D, rot, rope->style, rope->cos,
-                                  rope->sin, strm);
+  // When the call takes the persistent kernel and turns the whole head rotate-half, Q is
+  // turned in its registers as it is read and only K goes through the rotation pass.
+  int nqt = 0;
+  int64_t P = 0;
+  const bool fuse_q = rope->style == 0 && rot == D &&
+                      persist_plan(q, k, v, p.mask_kind, is_causal ? 1 : 0, lse != nullptr, Lk, true,
+                                   &nqt, &P) != nullptr;
+  wf::RopeDesc dq = desc(q, &qr, rope->q_pos0);
+  if (fuse_q) dq.B = 0;   // no Q rows in the pass
+  hipError_t he = wf::launch_rope(kernel_dtype(q->dtype), dq, desc(k, &kr, rope->k_pos0), (int)D,
+                                  rot, rope->style, rope->cos, rope->sin, strm);
   if (he != hipSuccess) return hip_status(he, "rope launch");
+  if (fuse_q)
+    return run_dense(q, &kr, v, mask, p.mask_kind, p.mask_vec, p.mask_lds, is_causal ? 1 : 0,
+                     p.scale, out, lse, Lk, strm, rope);
   return run_dense(&qr, &kr, v, mask, p.mask_kind, p.mask_vec, p.mask_lds, is_causal ? 1 : 0,
                    p.scale, out, lse, Lk, strm);
 }

@@ -26,6 +26,8 @@ const AttnEntry* attn_table_sdpa_bf16_d128(int* n);
 const AttnEntry* attn_table_sdpa_f16_d64(int* n);
 const AttnEntry* attn_table_sdpa_f16_d128(int* n);
 const AttnEntry* attn_table_mla(int* n);
+const AttnEntry* attn_table_p_rope_bf16(int* n);
+const AttnEntry* attn_table_p_rope_f16(int* n);
 const AttnEntry* attn_table_split_bf16(int* n);
 const AttnEntry* attn_table_split_f16(int* n);
 const AttnEntry* attn_table_splitp_bf16(int* n);
@@ -57,6 +59,10 @@ const AttnEntry* attn_table_p_f16_d64(int* n);
   {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL, SUM16 ? MODE_DENSE_P16 : MODE_DENSE_P,      \
    (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL, SUM16>,                             \
    AttnFwdP<T, D, D, HPW, CAUSAL, SUM16>::BMP, 64}
+#define WF_ATTN_PR_ENTRY(T, DT, D, HPW, CAUSAL, SUM16)                                       \
+  {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL, SUM16 ? MODE_DENSE_PR16 : MODE_DENSE_PR,    \
+   (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL, SUM16, true>,                       \
+   AttnFwdP<T, D, D, HPW, CAUSAL, SUM16, true>::BMP, 64}
 constexpr int kPersistMaxItems = AttnFwdP<__bf16, 128, 128, 4, false, false>::MAX_ITEMS;
 
 // fp32 path (MFMA 32x32x2 f32).

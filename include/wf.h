@@ -103,8 +103,11 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
  *   (x_a, x_b) -> (x_a cos - x_b sin, x_b cos + x_a sin),
  * pairs (i, i + rot_dim/2) for style 0 (rotate-half) or (2i, 2i + 1) for style 1
  * (interleaved). Query row r sits at position q_pos0 + r, key row j at k_pos0 + j; v is not
- * rotated. One launch writes rotated contiguous copies of q and k into `workspace`, then the
- * attention of wf_sdpa_fwd runs on them (same masks, causal rule, lse, dtypes, head dims).
+ * rotated. One launch writes a rotated contiguous copy of k, and of q, into `workspace`, then
+ * the attention of wf_sdpa_fwd runs on them (same masks, causal rule, lse, dtypes, head dims).
+ * When the call takes the persistent kernel (16-bit, no mask) with style 0 over the whole
+ * head, q is instead turned inside that kernel as it is read (fp32, rounded once), and only k
+ * is copied; the workspace size does not depend on which happens.
  *   rope->cos, rope->sin  device fp32 [max_pos, rot_dim/2], contiguous, 16-byte aligned;
  *   rot_dim 0 (no rotation) or a multiple of 16 up to the head dim; positions must lie in the
  *   table. workspace: at least wf_sdpa_rope_workspace_size(q, k) bytes, 256-byte aligned.
