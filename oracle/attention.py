@@ -42,6 +42,14 @@ MASK_NONE = 0
 MASK_CAUSAL = 1
 
 
+def _heads(x, H, lead):
+    """[*lead axes, H*d] or [*lead axes, H, d] -> [*lead axes, H, d]. The head width is
+    computed rather than inferred, so a tensor with no tokens keeps its shape too."""
+    if x.ndim == lead + 1:
+        return x.reshape(x.shape[:lead] + (H, x.shape[lead] // H))
+    return x.reshape(x.shape[:lead] + (H, x.shape[-1]))
+
+
 def _f64(x):
     """Exact upcast of a torch tensor or array to a float64 numpy array."""
     if x is None:
@@ -153,29 +161,20 @@ def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num,
     if mask_type not in (MASK_NONE, MASK_CAUSAL):
         raise ValueError("mask_type must be 0 (none) or 1 (causal)")
     G = Hq // Hkv
-    q = _f64(q)
-    q = q.reshape(q.shape[0], Hq, -1)
-    qr = _f64(q_rope).reshape(q.shape[0], Hq, -1)
+    q = _heads(_f64(q), Hq, 1)
+    qr = _heads(_f64(q_rope), Hq, 1)
     cq, ck = cu_seqlens(q_seqlen), cu_seqlens(kv_seqlen)
     if len(cq) != len(ck):
         raise ValueError("qSeqLen and kvSeqLen lengths differ")
     if kv_layout == "packed":
-        k = _f64(k)
-        k = k.reshape(k.shape[0], Hkv, -1)
-        kr = _f64(k_rope).reshape(k.shape[0], Hkv, -1)
-        v = _f64(v)
-        v = v.reshape(v.shape[0], Hkv, -1)
+        k, kr, v = (_heads(_f64(t), Hkv, 1) for t in (k, k_rope, v))
         if ck[-1] > k.shape[0]:
             raise ValueError("sequence lengths exceed the packed token count")
 
         def kv_rows(i):  # sequence i's keys, rotary keys and values [lk, Hkv, d]
             return k[ck[i]:ck[i + 1]], kr[ck[i]:ck[i + 1]], v[ck[i]:ck[i + 1]]
     elif kv_layout == "padded":
-        k = _f64(k)
-        k = k.reshape(k.shape[0], k.shape[1], Hkv, -1)
-        kr = _f64(k_rope).reshape(k.shape[0], k.shape[1], Hkv, -1)
-        v = _f64(v)
-        v = v.reshape(v.shape[0], v.shape[1], Hkv, -1)
+        k, kr, v = (_heads(_f64(t), Hkv, 2) for t in (k, k_rope, v))
         if k.shape[0] != len(ck) - 1:
             raise ValueError("padded K/V need one batch entry per sequence")
         if len(ck) > 1 and np.diff(ck).max() > k.shape[1]:

@@ -252,6 +252,23 @@ def test_mla_padded_kv_rejects_long_sequence():
                            kv_layout="padded")
 
 
+@pytest.mark.parametrize("layout", ["packed", "padded"])
+def test_mla_without_tokens_and_without_keys(layout):
+    # no query tokens at all: an empty [0, Hq, Dv] result, flat or 3-D inputs alike; a
+    # sequence without keys: its rows are 0 (fully masked rows give 0)
+    q, qr, k, kr, v = _mla_inputs([0, 0], [3, 0], 2, 1)
+    if layout == "padded":
+        k, kr, v = (torch.stack([t, torch.zeros_like(t)]) for t in (k, kr, v))
+    for qq, qqr in ((q, qr), (q.reshape(0, 2 * 16), qr.reshape(0, 2 * 8))):
+        out = varlen_mla_prefill(qq, qqr, k, kr, v, [0, 0], [3, 0], 2, 1, 0.3, 1, kv_layout=layout)
+        assert out.shape == (0, 2, v.shape[-1])
+    q, qr, k, kr, v = _mla_inputs([2, 3], [2, 0], 2, 1)
+    if layout == "padded":
+        k, kr, v = (torch.stack([t, torch.zeros_like(t)]) for t in (k, kr, v))
+    out = varlen_mla_prefill(q, qr, k, kr, v, [2, 3], [2, 0], 2, 1, 0.3, 0, kv_layout=layout)
+    assert np.all(out[2:] == 0) and np.all(np.isfinite(out[:2])) and np.any(out[:2] != 0)
+
+
 def test_mla_flat_layout_equals_3d_layout():
     lengths = [3, 9]
     q, qr, k, kr, v = _mla_inputs(lengths, lengths, 2, 2)
