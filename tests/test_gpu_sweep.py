@@ -13,7 +13,7 @@ from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-N_CASES = 100
+N_CASES = 300
 
 
 def _case(i):
@@ -74,7 +74,7 @@ def test_random_case(i):
 
 # ---------------------------------------------------------------- decode --------------------
 
-@pytest.mark.parametrize("i", range(30))
+@pytest.mark.parametrize("i", range(80))
 def test_random_decode(i):
     r = np.random.default_rng(5000 + i)
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[str(r.choice(["bf16", "fp16"]))]
@@ -102,7 +102,7 @@ def test_random_decode(i):
 
 # ---------------------------------------------------------------- MLA prefill ---------------
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(40))
 def test_random_mla(i):
     r = np.random.default_rng(7000 + i)
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[str(r.choice(["bf16", "fp16"]))]
@@ -140,7 +140,7 @@ def test_random_mla(i):
 
 # ---------------------------------------------------------------- RoPE ----------------------
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(40))
 def test_random_rope(i):
     r = np.random.default_rng(9000 + i)
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[str(r.choice(["bf16", "fp16"]))]
@@ -169,7 +169,7 @@ def test_random_rope(i):
 
 # ---------------------------------------------------------------- block KV cache attend -----
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(16))
 def test_random_cache_attend(i):
     from exact_attention_forward_flash_amd import BlockKVCache
     r = np.random.default_rng(11000 + i)
