@@ -333,6 +333,7 @@ constexpr int kMaxSplits = 16;
 // that about kDecodeGroups work groups stream K/V at once. It depends on shapes only, so the
 // workspace size does not depend on the device.
 constexpr int kMaxDecodeSplits = 256;
+constexpr int64_t kDecodeMinGroups = 256;
 constexpr int64_t kDecodeGroups = 512;
 struct DecodePlan {
   const wf::AttnEntry* e = nullptr;
@@ -358,12 +359,17 @@ DecodePlan decode_plan(int dt, int64_t B, int64_t Hq, int64_t Hkv, int64_t Lq, i
   p.base = (int64_t)p.n_qt * B * Hkv * (p.pack ? 1 : G / hpw);
   const int64_t base = std::max<int64_t>(1, p.base);
   const int64_t n_kt = (Lk + p.e->bn - 1) / p.e->bn;
-  int64_t groups = kDecodeGroups, min_tiles = 2;
+  // About kDecodeGroups groups, but splits of at least min_tiles tiles unless that leaves
+  // fewer than kDecodeMinGroups (measured: multi-query decode, 8 KV groups over 16k keys,
+  // 0.056 ms with 64 splits of 4 tiles, 0.038 ms with 16 of 16; the per-split start-up and
+  // the merge outweigh the extra parallelism on short per-group K/V).
+  int64_t groups = kDecodeGroups, min_tiles = 16;
   if (const char* t = getenv("WF_TUNE_DECODE_GROUPS")) groups = std::max(1, atoi(t));
   if (const char* t = getenv("WF_TUNE_DECODE_MIN_TILES")) min_tiles = std::max(1, atoi(t));
   int64_t n = (groups + base - 1) / base;
+  n = std::min<int64_t>(n, std::max<int64_t>(1, n_kt / min_tiles));
+  n = std::max<int64_t>(n, std::min<int64_t>((kDecodeMinGroups + base - 1) / base, n_kt));
   n = std::min<int64_t>(n, kMaxDecodeSplits);
-  n = std::min<int64_t>(n, std::max<int64_t>(1, n_kt / min_tiles));  // tiles per split
   p.tps = (int)std::max<int64_t>(1, (n_kt + n - 1) / n);
   p.n_splits = (int)std::max<int64_t>(1, (n_kt + p.tps - 1) / p.tps);
   return p;
@@ -848,9 +854,10 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
   const int64_t base_blocks = (int64_t)n_qt * B * Hkv * (G / hpw);
   const int cus = device_cus();
-  // About one work group per CU: measured on the 256-query chunk over a 4k window, 192-384
-  // groups run 20% faster than 512 (fewer fp32 partials to write and merge).
-  int64_t target = cus;
+  // About 3/4 of a work group per CU: measured on the 256-query chunk over a 4k window (256
+  // CUs), 192 groups run 20% faster than 512 (fewer fp32 partials to write and merge) and
+  // ~4% faster than 256.
+  int64_t target = std::max(1, cus * 3 / 4);
   if (const char* t = getenv("WF_TUNE_ATTEND_GROUPS")) target = std::max(1, atoi(t));
   int n_splits = (int)((target + base_blocks - 1) / base_blocks);
   if (n_splits > kMaxSplits) n_splits = kMaxSplits;
