@@ -38,9 +38,11 @@ enum { MASK_NONE = 0, MASK_BOOL = 1, MASK_HALF = 2, MASK_F32 = 3 };
 // (attn_fwd_p.hpp) with fp32 row sums and with row sums over the 16-bit weights.
 // MODE_SPLITP: split-KV with the G*Lq (query head, position) rows of a KV head packed into
 // the query rows of the tiles (row r = head r / Lq, position r % Lq), for few queries per head.
-// MODE_DENSE_PR / MODE_DENSE_PR16: the persistent kernel that turns Q by a rotary table.
+// MODE_DENSE_PR / MODE_DENSE_PR16: the persistent kernel that turns Q by a rotate-half table;
+// MODE_DENSE_PI / MODE_DENSE_PI16: by an interleaved one.
 enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3, MODE_DENSE_P16 = 4,
-       MODE_SPLITP = 5, MODE_DENSE_PR = 6, MODE_DENSE_PR16 = 7 };
+       MODE_SPLITP = 5, MODE_DENSE_PR = 6, MODE_DENSE_PR16 = 7, MODE_DENSE_PI = 8,
+       MODE_DENSE_PI16 = 9 };
 
 struct FwdArgs {
   const void* q; const void* q2; const void* k; const void* k2; const void* v;
@@ -64,10 +66,11 @@ struct FwdArgs {
   int xcd_parts;      // work split over the 8 XCDs by KV head (counter[16 + 4x] for XCD x)
   // split-KV mode
   int tiles_per_split; float* part_o; float* part_lse;
-  // rotate-half rotary embedding of Q over the whole head as it is read (persistent ROPE
-  // kernels): query row i turns pair d by rq_cos[i][d], rq_sin[i][d] (rows of head dim / 2
-  // floats, already offset to the first query's position)
+  // rotary embedding of Q as it is read (persistent ROPE kernels): query row i turns pair d by
+  // rq_cos[i][d], rq_sin[i][d] (rows of rq_rot / 2 floats, already offset to the first query's
+  // position); rotate-half kernels take rq_rot = head dim
   const float* rq_cos; const float* rq_sin;
+  int rq_rot;
 };
 
 struct WorkItem {

@@ -21,8 +21,9 @@
 // KV group on one XCD) in rounds over the XCD's P/8 groups, alternating direction each round,
 // which pairs long and short causal items on every CU.
 //
-// ROPE instantiations turn Q by a rotate-half rotary table over the whole head as it is read
-// into registers (once per item), so that such calls need a separate pass over K only.
+// ROPE instantiations turn Q by a rotary table as it is read into registers (once per item):
+// rotate-half over the whole head (1) or interleaved over the first rq_rot dims (2), so that
+// such calls need a separate pass over K only.
 //
 // Every wave of a group must compute the same tiles, so for causal calls the group covers
 // one 64-key tile's worth of positions (BMP == BN, HPW = 4 with 8 waves) and the causal
@@ -34,7 +35,7 @@ namespace wf {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16, bool ROPE = false>
+template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16, int ROPE = 0>
 struct AttnFwdP {
   static constexpr int NW = 8;
   static constexpr int BN = 64;
@@ -192,9 +193,10 @@ struct AttnFwdP {
     // error up to ~1e-3, as large as the output's own rounding). Calls that ask for the lse
     // therefore keep Q as it is and scale every score in fp32.
     //
-    // ROPE: Q is turned first (rotate-half over all DQK dims), in fp32, and rounded once. Both
-    // members of every pair sit in the lane's own registers (chunk s pairs with chunk
-    // s + NS/2). The table rows are read from global memory (they stay in L2: one row per
+    // ROPE (1: rotate-half over all DQK dims, 2: interleaved over the first rq_rot dims): Q is
+    // turned first, in fp32, and rounded once. Both members of every pair sit in the lane's
+    // own registers (rotate-half: chunk s pairs with chunk s + NS/2; interleaved: adjacent
+    // elements of a chunk, and rq_rot % 16 == 0 turns whole chunks for both half-waves). The table rows are read from global memory (they stay in L2: one row per
     // query position, shared by every head and batch).
     u32x4 qf[NS];
     auto read_q = [&](const Item& it) {
@@ -217,7 +219,7 @@ struct AttnFwdP {
           for (int e = 0; e < 8; ++e) y[e] = PRESCALE ? (T)((float)x[e] * c) : x[e];
           qf[s] = __builtin_bit_cast(u32x4, y);
         }
-      } else {   // rotate-half over all DQK dims: chunk s pairs with chunk s + NS/2
+      } else if constexpr (ROPE == 1) {   // rotate-half over all DQK dims: chunk s pairs with s + NS/2
         int p = it.pos0 + qw + j;
         p = p < a.Lq ? p : a.Lq - 1;   // rows past Lq are not stored; keep their reads in the table
         const float* cr = a.rq_cos + (int64_t)p * (DQK / 2);
@@ -238,6 +240,30 @@ struct AttnFwdP {
           }
           put(s, ya);
           put(s + NS / 2, yb);
+        }
+      } else {   // interleaved over the first rq_rot dims: pairs (2i, 2i + 1) inside a chunk
+        const int half = a.rq_rot >> 1, nrs = a.rq_rot >> 4;   // chunks s < nrs turn
+        int p = it.pos0 + qw + j;
+        p = p < a.Lq ? p : a.Lq - 1;
+        const float* cr = a.rq_cos + (int64_t)p * half;
+        const float* sr = a.rq_sin + (int64_t)p * half;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const v8 x = chunk(s);
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = (float)x[e];
+          if (s < nrs) {
+            const int i0 = 8 * s + 4 * hf;
+            const f32x4 c4 = *(const f32x4*)(cr + i0), s4 = *(const f32x4*)(sr + i0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float fa = y[2 * i], fb = y[2 * i + 1];
+              y[2 * i] = fmaf(fa, c4[i], -fb * s4[i]);
+              y[2 * i + 1] = fmaf(fb, c4[i], fa * s4[i]);
+            }
+          }
+          put(s, y);
         }
       }
     };
@@ -592,7 +618,7 @@ struct AttnFwdP {
   }
 };
 
-template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16, bool ROPE = false>
+template <typename T, int DQK, int DV, int HPW, bool CAUSAL, bool SUM16, int ROPE = 0>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_p_kernel(FwdArgs a) {
   typedef AttnFwdP<T, DQK, DV, HPW, CAUSAL, SUM16, ROPE> K;

@@ -3,12 +3,13 @@
 // bf16, head dims 64 and 128.
 #include "wf_internal.hpp"
 namespace wf {
-#define E(D, HPW, CAUSAL, SUM16) WF_ATTN_PR_ENTRY(__bf16, DT_BF16, D, HPW, CAUSAL, SUM16)
+#define E(D, HPW, CAUSAL, SUM16, ROPE) WF_ATTN_PR_ENTRY(__bf16, DT_BF16, D, HPW, CAUSAL, SUM16, ROPE)
+// ROPE 1: rotate-half over the whole head.
 static const AttnEntry kTable[] = {
-    E(128, 1, false, true),  E(128, 2, false, true),  E(128, 4, false, true),  E(128, 4, true, true),
-    E(128, 1, false, false), E(128, 2, false, false), E(128, 4, false, false), E(128, 4, true, false),
-    E(64, 1, false, true),   E(64, 2, false, true),   E(64, 4, false, true),   E(64, 4, true, true),
-    E(64, 1, false, false),  E(64, 2, false, false),  E(64, 4, false, false),  E(64, 4, true, false),
+    E(128, 1, false, true, 1),  E(128, 2, false, true, 1),  E(128, 4, false, true, 1),  E(128, 4, true, true, 1),
+    E(128, 1, false, false, 1), E(128, 2, false, false, 1), E(128, 4, false, false, 1), E(128, 4, true, false, 1),
+    E(64, 1, false, true, 1),  E(64, 2, false, true, 1),  E(64, 4, false, true, 1),  E(64, 4, true, true, 1),
+    E(64, 1, false, false, 1), E(64, 2, false, false, 1), E(64, 4, false, false, 1), E(64, 4, true, false, 1),
 };
 #undef E
 const AttnEntry* attn_table_p_rope_bf16(int* n) {

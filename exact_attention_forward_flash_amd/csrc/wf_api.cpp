@@ -119,7 +119,8 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
                                    wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128,
                                    wf::attn_table_p_bf16_d64,    wf::attn_table_p_bf16_d128,
                                    wf::attn_table_p_f16_d64,     wf::attn_table_p_f16_d128,
-                                   wf::attn_table_p_rope_bf16,   wf::attn_table_p_rope_f16};
+                                   wf::attn_table_p_rope_bf16,   wf::attn_table_p_rope_f16,
+                                   wf::attn_table_p_ropei_bf16,  wf::attn_table_p_ropei_f16};
   for (TableFn f : tables) {
     int n = 0;
     const wf::AttnEntry* t = f(&n);
@@ -191,11 +192,11 @@ int resolve_scale(float scale, int64_t dqk, float* out) {
 // items): calls without a mask whose Q/K/V copy offsets fit in 32 bits and, when causal, whose
 // work groups cover one 64-key tile of query positions (HPW = 4). Returns the table entry and
 // sets the query-tile count and the grid, or returns nullptr when the call takes the
-// one-item-per-group kernels. rope: the variant that turns Q by a rotary table.
-// WF_TUNE_PERSIST=0 turns it off.
+// one-item-per-group kernels. rope: 0, or the variant that turns Q by a rotary table
+// (1 rotate-half over the whole head, 2 interleaved). WF_TUNE_PERSIST=0 turns it off.
 static const wf::AttnEntry* persist_plan(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
                                          int mask_kind, int causal, bool has_lse, int64_t Lk,
-                                         bool rope, int* n_qtiles, int64_t* grid) {
+                                         int rope, int* n_qtiles, int64_t* grid) {
   const int dt = kernel_dtype(q->dtype);
   if (dt == wf::DT_F32 || mask_kind != wf::MASK_NONE || Lk <= 0) return nullptr;
   const int B = (int)q->shape[0], Hq = (int)q->shape[1], Lq = (int)q->shape[2];
@@ -211,8 +212,9 @@ static const wf::AttnEntry* persist_plan(const wf_tensor* q, const wf_tensor* k,
   if (!persist) return nullptr;
   // Without the lse the row sums are taken over the 16-bit weights (exactly the weights
   // that multiply V; their sum keeps the 16-bit rounding, which the lse would show).
-  const int pmode = rope ? (has_lse ? wf::MODE_DENSE_PR : wf::MODE_DENSE_PR16)
-                         : (has_lse ? wf::MODE_DENSE_P : wf::MODE_DENSE_P16);
+  const int pmode = rope == 1   ? (has_lse ? wf::MODE_DENSE_PR : wf::MODE_DENSE_PR16)
+                    : rope == 2 ? (has_lse ? wf::MODE_DENSE_PI : wf::MODE_DENSE_PI16)
+                                : (has_lse ? wf::MODE_DENSE_P : wf::MODE_DENSE_P16);
   const wf::AttnEntry* pe = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, wf::MASK_NONE, causal, pmode);
   const int ncu = cu_count();
   if (pe == nullptr || ncu <= 0) return nullptr;
@@ -225,9 +227,9 @@ static const wf::AttnEntry* persist_plan(const wf_tensor* q, const wf_tensor* k,
 }
 
 // Dense attention over already validated operands (shared by SDPA and the cache attend when
-// a single split suffices). mask_kind: wf::MASK_*. rope_q: turn Q by this rotate-half table
-// over the whole head on its way into the persistent kernel (the caller has checked with
-// persist_plan that the call takes it).
+// a single split suffices). mask_kind: wf::MASK_*. rope_q: turn Q by this rotary table on
+// its way into the persistent kernel (the caller has checked with persist_plan that the call
+// takes it).
 int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const wf_tensor* mask,
               int mask_kind, bool mask_vec, bool mask_lds, int causal, float scale, wf_tensor* out, float* lse,
               int64_t Lk, hipStream_t stream, const wf_rope* rope_q = nullptr) {
@@ -273,14 +275,16 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   {
     int nqt = 0;
     int64_t P = 0;
-    const wf::AttnEntry* pe = persist_plan(q, k, v, mask_kind, causal, lse != nullptr, Lk,
-                                           rope_q != nullptr, &nqt, &P);
+    const int rk = rope_q == nullptr ? 0 : rope_q->style == 0 ? 1 : 2;
+    const wf::AttnEntry* pe = persist_plan(q, k, v, mask_kind, causal, lse != nullptr, Lk, rk,
+                                           &nqt, &P);
     if (pe != nullptr) {
       a.n_qtiles = nqt;
       if (rope_q != nullptr) {
         const int64_t row0 = rope_q->q_pos0 * (rope_q->rot_dim / 2);
         a.rq_cos = rope_q->cos + row0;
         a.rq_sin = rope_q->sin + row0;
+        a.rq_rot = rope_q->rot_dim;
       }
       return hip_status(launch(pe->fn, dim3((unsigned)P), dim3(512), a, stream), "attention launch");
     }
@@ -554,13 +558,14 @@ int wf_sdpa_rope_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
     return d;
   };
   hipStream_t strm = (hipStream_t)stream;
-  // When the call takes the persistent kernel and turns the whole head rotate-half, Q is
-  // turned in its registers as it is read and only K goes through the rotation pass.
+  // When the call takes the persistent kernel (rotate-half over the whole head, or
+  // interleaved), Q is turned in its registers as it is read and only K goes through the
+  // rotation pass.
   int nqt = 0;
   int64_t P = 0;
-  const bool fuse_q = rope->style == 0 && rot == D &&
-                      persist_plan(q, k, v, p.mask_kind, is_causal ? 1 : 0, lse != nullptr, Lk, true,
-                                   &nqt, &P) != nullptr;
+  const bool fuse_q = (rope->style == 1 || rot == D) &&
+                      persist_plan(q, k, v, p.mask_kind, is_causal ? 1 : 0, lse != nullptr, Lk,
+                                   rope->style == 0 ? 1 : 2, &nqt, &P) != nullptr;
   wf::RopeDesc dq = desc(q, &qr, rope->q_pos0);
   if (fuse_q) dq.B = 0;   // no Q rows in the pass
   hipError_t he = wf::launch_rope(kernel_dtype(q->dtype), dq, desc(k, &kr, rope->k_pos0), (int)D,

@@ -28,6 +28,8 @@ const AttnEntry* attn_table_sdpa_f16_d128(int* n);
 const AttnEntry* attn_table_mla(int* n);
 const AttnEntry* attn_table_p_rope_bf16(int* n);
 const AttnEntry* attn_table_p_rope_f16(int* n);
+const AttnEntry* attn_table_p_ropei_bf16(int* n);
+const AttnEntry* attn_table_p_ropei_f16(int* n);
 const AttnEntry* attn_table_split_bf16(int* n);
 const AttnEntry* attn_table_split_f16(int* n);
 const AttnEntry* attn_table_splitp_bf16(int* n);
@@ -59,10 +61,12 @@ const AttnEntry* attn_table_p_f16_d64(int* n);
   {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL, SUM16 ? MODE_DENSE_P16 : MODE_DENSE_P,      \
    (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL, SUM16>,                             \
    AttnFwdP<T, D, D, HPW, CAUSAL, SUM16>::BMP, 64}
-#define WF_ATTN_PR_ENTRY(T, DT, D, HPW, CAUSAL, SUM16)                                       \
-  {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL, SUM16 ? MODE_DENSE_PR16 : MODE_DENSE_PR,    \
-   (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL, SUM16, true>,                       \
-   AttnFwdP<T, D, D, HPW, CAUSAL, SUM16, true>::BMP, 64}
+// ROPE 1 (rotate-half) or 2 (interleaved): the persistent kernel that turns Q as it reads it.
+#define WF_ATTN_PR_ENTRY(T, DT, D, HPW, CAUSAL, SUM16, ROPE)                                 \
+  {DT, D, D, D, 8, 32, HPW, MASK_NONE, CAUSAL,                                              \
+   ROPE == 1 ? (SUM16 ? MODE_DENSE_PR16 : MODE_DENSE_PR) : (SUM16 ? MODE_DENSE_PI16 : MODE_DENSE_PI), \
+   (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL, SUM16, ROPE>,                       \
+   AttnFwdP<T, D, D, HPW, CAUSAL, SUM16, ROPE>::BMP, 64}
 constexpr int kPersistMaxItems = AttnFwdP<__bf16, 128, 128, 4, false, false>::MAX_ITEMS;
 
 // fp32 path (MFMA 32x32x2 f32).

@@ -106,8 +106,8 @@ int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
  * rotated. One launch writes a rotated contiguous copy of k, and of q, into `workspace`, then
  * the attention of wf_sdpa_fwd runs on them (same masks, causal rule, lse, dtypes, head dims).
  * When the call takes the persistent kernel (16-bit, no mask) with style 0 over the whole
- * head, q is instead turned inside that kernel as it is read (fp32, rounded once), and only k
- * is copied; the workspace size does not depend on which happens.
+ * head or with style 1, q is instead turned inside that kernel as it is read (fp32, rounded
+ * once), and only k is copied; the workspace size does not depend on which happens.
  *   rope->cos, rope->sin  device fp32 [max_pos, rot_dim/2], contiguous, 16-byte aligned;
  *   rot_dim 0 (no rotation) or a multiple of 16 up to the head dim; positions must lie in the
  *   table. workspace: at least wf_sdpa_rope_workspace_size(q, k) bytes, 256-byte aligned.

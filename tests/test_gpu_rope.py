@@ -52,12 +52,13 @@ def test_rope_shapes(case):
     assert np.abs(to64(lse)[live] - ref_lse[live]).max() < tol
 
 
-def test_rope_separate_pass_path(monkeypatch):
-    """The first case (rotate-half over the whole head, causal GQA) turns Q in the persistent
-    kernel's registers; with that kernel turned off its Q goes through the separate pass
-    instead, and both paths meet the bounds."""
+@pytest.mark.parametrize("case", [CASES[0], CASES[1]], ids=["rotate-half", "interleaved"])
+def test_rope_separate_pass_path(case, monkeypatch):
+    """These cases (rotate-half over the whole head, causal GQA; interleaved over half the
+    head) turn Q in the persistent kernel's registers; with that kernel turned off their Q goes
+    through the separate pass instead, and both paths meet the bounds."""
     monkeypatch.setenv("WF_TUNE_PERSIST", "0")
-    test_rope_shapes(CASES[0])
+    test_rope_shapes(case)
 
 
 @pytest.mark.parametrize("tab_std,lse", [(1.0, True), (0.5 ** 0.5, False)], ids=["N(0,1)+lse", "N(0,1/2)"])
