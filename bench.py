@@ -1,10 +1,16 @@
 """Throughput of exact attention forward on one MI355X: causal GQA prefill, bf16,
 B=4, Hq=32, Hkv=8, Lq=Lk=4096, head dim 128 (synthetic N(0,1) inputs, seed 7).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T] [--no-cpu-baseline]
 
 A step is one forward pass over the batch (one launch of the attention kernel) with the
-inputs already resident in HBM. Prints one JSON line with the throughput in TFLOP/s
+inputs already resident in HBM. Before the W warm-up steps the call runs back to back for T
+milliseconds of GPU time (default 300): the GPU's clock governor takes that long to settle
+after a fresh start (measured per launch on a fresh box: launches 0-2 0.55 ms, then 0.60-0.72
+ms over launches 3-30 while the clock drops, back to 0.55 by launch 35 and a steady 0.52 ms
+from about launch 100 on), so a timed region that starts a few launches into the process
+measures the governor, not the kernel. The settle phase is reported in the JSON line
+("clock_settle": launches and milliseconds). Prints one JSON line with the throughput in TFLOP/s
 (4*B*H*L^2*d, halved for causal), the fraction of the bf16 dense MFMA peak, the kernel's
 roofline figures (average launch time from HIP events on the launch stream) and the CPU
 oracle timed on a bounded sample of the same workload.
@@ -113,10 +119,28 @@ def write_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     print(json.dumps(rec))
 
 
-def _time_steps(step, steps, warmup, stream):
-    """Average milliseconds of step() over `steps` runs after `warmup`, from HIP events on the
-    launch stream."""
+def clock_settle(step, settle_ms, stream):
+    """Runs step() back to back until settle_ms of GPU time have passed (in blocks of 20
+    launches timed by HIP events on the launch stream); returns what was run."""
     import torch
+    n, spent = 0, 0.0
+    while spent < settle_ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(20):
+            step()
+        b.record(stream)
+        b.synchronize()
+        spent += a.elapsed_time(b)
+        n += 20
+    return {"launches": n, "ms": round(spent, 1)}
+
+
+def _time_steps(step, steps, warmup, stream, settle_ms=200.0):
+    """Average milliseconds of step() over `steps` runs after settle_ms of back-to-back launches
+    and `warmup` more, from HIP events on the launch stream."""
+    import torch
+    clock_settle(step, settle_ms, stream)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -258,10 +282,11 @@ def other_workload(name, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The GPU's clocks settle over the first few dozen launches (a launch takes ~0.6 ms):
-    # 100 untimed launches precede the 200 timed ones.
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="GPU milliseconds of back-to-back untimed launches before the warm-up "
+                         "steps, while the clock governor settles (reported as clock_settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="causal_gqa",
                     choices=["causal_gqa", "varlen_mla", "masked_bool", "masked_float",
@@ -323,6 +348,7 @@ def main():
             raise RuntimeError(lib.wf_last_error().decode())
 
     w_scale = 1.0 / (CFG["D"] ** 0.5)
+    settle = clock_settle(step, args.settle_ms, stream)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -358,6 +384,7 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel_ms": round(kernel_ms, 4)},
     }
+    line["clock_settle"] = settle
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

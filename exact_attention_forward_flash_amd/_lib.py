@@ -57,6 +57,8 @@ SIGNATURES = {
     "wf_block_kv_attend": (_i32, [_S, _T, _T, _T, _f, _T, _vp, _sz, _vp]),
     "wf_status_string": (ctypes.c_char_p, [_i32]),
     "wf_last_error": (ctypes.c_char_p, []),
+    "wf_tune_set": (_i32, [ctypes.c_char_p, _i32]),
+    "wf_tune_get": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]),
 }
 
 _lib = None

@@ -6,6 +6,7 @@ the library's HIP kernels on torch's current stream.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 
@@ -46,6 +47,24 @@ def _stream(t: torch.Tensor):
 
 def _scale(scale):
     return float("nan") if scale is None else float(scale)
+
+
+@contextlib.contextmanager
+def tune(**settings):
+    """Overrides the library's kernel choice for the calls inside the block (names and values
+    as wf_tune_set in include/wf.h; -1 = automatic), restoring the previous values after."""
+    lib = _lib.load()
+    old = {}
+    for name, value in settings.items():
+        cur = ctypes.c_int()
+        check(lib.wf_tune_get(name.encode(), ctypes.byref(cur)))
+        old[name] = cur.value
+        check(lib.wf_tune_set(name.encode(), int(value)))
+    try:
+        yield
+    finally:
+        for name, value in old.items():
+            lib.wf_tune_set(name.encode(), value)
 
 
 def sdpa(q, k, v, attn_mask=None, dropout_p=0.0, is_causal=False, scale=None,

@@ -40,9 +40,10 @@ enum { MASK_NONE = 0, MASK_BOOL = 1, MASK_HALF = 2, MASK_F32 = 3 };
 // the query rows of the tiles (row r = head r / Lq, position r % Lq), for few queries per head.
 // MODE_DENSE_PR / MODE_DENSE_PR16: the persistent kernel that turns Q by a rotate-half table;
 // MODE_DENSE_PI / MODE_DENSE_PI16: by an interleaved one.
+// MODE_DENSE_Q: the persistent 64-query-wave kernel (attn_fwd_q.hpp), calls without the lse.
 enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3, MODE_DENSE_P16 = 4,
        MODE_SPLITP = 5, MODE_DENSE_PR = 6, MODE_DENSE_PR16 = 7, MODE_DENSE_PI = 8,
-       MODE_DENSE_PI16 = 9 };
+       MODE_DENSE_PI16 = 9, MODE_DENSE_Q = 10 };
 
 struct FwdArgs {
   const void* q; const void* q2; const void* k; const void* k2; const void* v;

@@ -6,6 +6,7 @@
 #include "attn_fwd.hpp"
 #include "attn_fwd_w.hpp"
 #include "attn_fwd_p.hpp"
+#include "attn_fwd_q.hpp"
 
 namespace wf {
 
@@ -42,6 +43,8 @@ const AttnEntry* attn_table_p_bf16_d128(int* n);
 const AttnEntry* attn_table_p_bf16_d64(int* n);
 const AttnEntry* attn_table_p_f16_d128(int* n);
 const AttnEntry* attn_table_p_f16_d64(int* n);
+const AttnEntry* attn_table_q_bf16_d128(int* n);
+const AttnEntry* attn_table_q_f16_d128(int* n);
 
 #define WF_ATTN_ENTRY(T, DT, DQK, DQK1, DV, NW, HPW, MASK, CAUSAL, MODE)                     \
   {DT, DQK, DQK1, DV, NW, 32, HPW, MASK, CAUSAL, MODE,                                      \
@@ -68,6 +71,12 @@ const AttnEntry* attn_table_p_f16_d64(int* n);
    (const void*)&attn_fwd_p_kernel<T, D, D, HPW, CAUSAL, SUM16, ROPE>,                       \
    AttnFwdP<T, D, D, HPW, CAUSAL, SUM16, ROPE>::BMP, 64}
 constexpr int kPersistMaxItems = AttnFwdP<__bf16, 128, 128, 4, false, false>::MAX_ITEMS;
+// Persistent 64-query-wave kernel (4 waves, one per SIMD, no mask, no lse), built in
+// translation units that force the VGPR form of compiler-generated MFMAs.
+#define WF_ATTN_Q_ENTRY(T, DT, D, HPW, CAUSAL)                                               \
+  {DT, D, D, D, 4, 64, HPW, MASK_NONE, CAUSAL, MODE_DENSE_Q,                                \
+   (const void*)&attn_fwd_q_kernel<T, D, HPW, CAUSAL>, AttnFwdQ<T, D, HPW, CAUSAL>::BMP, 64}
+constexpr int kQMaxItems = AttnFwdQ<__bf16, 128, 4, false>::MAX_ITEMS;
 
 // fp32 path (MFMA 32x32x2 f32).
 struct F32Entry {

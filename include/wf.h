@@ -242,6 +242,22 @@ int wf_block_kv_attend(const wf_block_kv_state* st, const wf_tensor* q,
 const char* wf_status_string(int status);
 const char* wf_last_error(void);
 
+/* Kernel-selection overrides, for tests that must reach every kernel shape and for tuning
+ * (not part of the pages' operation; every setting computes the same attention).
+ * Process-wide values, initialised once from the environment variables WF_TUNE_<NAME>
+ * (upper-case name) on first use, then changed only here; -1 restores the automatic choice.
+ * Names: "hpw" (query heads per work group), "persist" (0: no persistent 32-query kernel),
+ * "q64" (1: the persistent 64-query-wave kernel where it applies; off by default), "qpw" (32 | 64: queries per wave of the
+ * one-item-per-group kernels), "nw" (4: waves per group of the 32-query kernel),
+ * "decode_pack" (0: no (head, position) row packing in wf_sdpa_decode), "decode_groups",
+ * "decode_min_tiles" (split plan of wf_sdpa_decode), "mla_xcd" (0: no per-XCD split of the
+ * MLA prefill), "attend_groups" (split plan of wf_block_kv_attend). Changing a value while
+ * another thread launches work races with that launch's choice (never with its result's
+ * correctness). Returns WF_ERR_UNSUPPORTED for an unknown name, WF_ERR_NULL for a NULL
+ * value pointer. */
+int wf_tune_set(const char* name, int value);
+int wf_tune_get(const char* name, int* value);
+
 #ifdef __cplusplus
 }
 #endif

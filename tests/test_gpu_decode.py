@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_flash_amd import WfError, sdpa, sdpa_decode, sdpa_decode_workspace_size
+from exact_attention_forward_flash_amd import WfError, sdpa, sdpa_decode, sdpa_decode_workspace_size, tune
 from synth import random_sdpa_inputs
 from tests.parity import assert_close, to64
 
@@ -88,10 +88,10 @@ def test_decode_bench_shape_sampled():
         assert_close(out[b:b + 1], ref, torch.bfloat16, f"batch {b}")
 
 
-def test_packed_rows_match_unpacked(monkeypatch):
+def test_packed_rows_match_unpacked():
     # the same call with (head, position) packing turned off agrees within rounding
     w = random_sdpa_inputs(2, 32, 2, 2, 3000, 128, 128, "bf16", seed=8)
     packed = _run(w, True)
-    monkeypatch.setenv("WF_TUNE_DECODE_PACK", "0")
-    plain = _run(w, True)
+    with tune(decode_pack=0):
+        plain = _run(w, True)
     assert (packed.float() - plain.float()).abs().max().item() < 2e-2

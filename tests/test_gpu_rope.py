@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_flash_amd import WfError, flattened_sdpa, sdpa, sdpa_rope
+from exact_attention_forward_flash_amd import WfError, flattened_sdpa, sdpa, sdpa_rope, tune
 from synth import causal_gqa_prefill, random_sdpa_inputs
 from tests.parity import assert_close, to64
 
@@ -53,12 +53,12 @@ def test_rope_shapes(case):
 
 
 @pytest.mark.parametrize("case", [CASES[0], CASES[1]], ids=["rotate-half", "interleaved"])
-def test_rope_separate_pass_path(case, monkeypatch):
+def test_rope_separate_pass_path(case):
     """These cases (rotate-half over the whole head, causal GQA; interleaved over half the
     head) turn Q in the persistent kernel's registers; with that kernel turned off their Q goes
     through the separate pass instead, and both paths meet the bounds."""
-    monkeypatch.setenv("WF_TUNE_PERSIST", "0")
-    test_rope_shapes(case)
+    with tune(persist=0):
+        test_rope_shapes(case)
 
 
 @pytest.mark.parametrize("tab_std,lse", [(1.0, True), (0.5 ** 0.5, False)], ids=["N(0,1)+lse", "N(0,1/2)"])

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_flash_amd import sdpa, WfError
+from exact_attention_forward_flash_amd import sdpa, tune, WfError
 from synth import causal_gqa_prefill, masked_sdpa_inputs, page_example_fp32, random_sdpa_inputs
 from tests.parity import assert_close, to64
 
@@ -126,10 +126,12 @@ def test_fully_masked_rows_and_empty_keys():
 
 
 # Every kernel shape on every case, whatever the default choice for it: the persistent
-# 32-query kernel (one work group per CU walking a list of work items; calls without a mask,
-# causal ones with four query heads per KV head), and the one-item-per-group kernels with
-# 64-query waves (one per SIMD, row sums over the 16-bit weights) and 32-query waves (two per
-# SIMD). The shape is picked per call from WF_TUNE_PERSIST and WF_TUNE_QPW.
+# 64-query-wave kernel (one wave per SIMD, one work group per CU walking a list of work items;
+# calls without a mask or lse, head dim 128, causal ones with four query heads per KV head),
+# the persistent 32-query kernel (calls without a mask), and the one-item-per-group kernels
+# with 64-query waves (one per SIMD, row sums over the 16-bit weights) and 32-query waves (two
+# per SIMD). The shape is picked per call through the library's tuning overrides; a call a
+# shape does not take falls through to the next one in that order.
 SHAPE_CASES = [c + (m,) for c in CASES for m in (None,)] + [
     ("bf16", 2, 4, 4, 130, 301, 128, False, "bool"),
     ("fp16", 2, 4, 4, 97, 200, 64, False, "half"),
@@ -137,17 +139,17 @@ SHAPE_CASES = [c + (m,) for c in CASES for m in (None,)] + [
 ]
 
 
-def _pick_shape(monkeypatch, shape):
+def _pick_shape(shape):
+    if shape == "q64p":
+        return tune(q64=1, persist=-1, qpw=-1)
     if shape == "persistent":
-        monkeypatch.setenv("WF_TUNE_PERSIST", "1")
-    else:
-        monkeypatch.setenv("WF_TUNE_PERSIST", "0")
-        monkeypatch.setenv("WF_TUNE_QPW", str(shape))
+        return tune(q64=0, persist=1, qpw=-1)
+    return tune(q64=0, persist=0, qpw=int(shape))
 
 
-@pytest.mark.parametrize("qpw", ["persistent", 64, 32])
+@pytest.mark.parametrize("qpw", ["q64p", "persistent", 64, 32])
 @pytest.mark.parametrize("case", SHAPE_CASES, ids=[str(c) for c in SHAPE_CASES])
-def test_kernel_shapes(case, qpw, monkeypatch):
+def test_kernel_shapes(case, qpw):
     dt, B, Hq, Hkv, Lq, Lk, D, causal, mkind = case
     w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 997)
     if mkind is not None:
@@ -155,8 +157,8 @@ def test_kernel_shapes(case, qpw, monkeypatch):
         w["mask"] = _mask(mkind, "b1", B, Hq, Lq, Lk, w["q"].dtype, g)
     ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w.get("mask"), is_causal=causal,
                          scale=np.float32(w["scale"]))
-    _pick_shape(monkeypatch, qpw)
-    out = run(w, is_causal=causal)
+    with _pick_shape(qpw):
+        out = run(w, is_causal=causal)
     assert_close(out, ref, w["q"].dtype, f"{case} {qpw}")
 
 
@@ -173,17 +175,18 @@ PERSIST_CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, causal
 ]
 
 
+@pytest.mark.parametrize("kernel", ["q64p", "persistent"])
 @pytest.mark.parametrize("case", PERSIST_CASES, ids=[str(c) for c in PERSIST_CASES])
-def test_persistent_many_items(case, monkeypatch):
+def test_persistent_many_items(case, kernel):
     dt, B, Hq, Hkv, Lq, Lk, D, causal = case
-    monkeypatch.setenv("WF_TUNE_PERSIST", "1")
     w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 991)
     ref, ref_lse = oracle.sdpa(w["q"], w["k"], w["v"], is_causal=causal, scale=np.float32(w["scale"]))
-    out, lse = run(w, is_causal=causal, return_lse=True)   # fp32 row sums, Q as given
-    assert_close(out, ref, w["q"].dtype, str(case))
-    assert np.abs(to64(lse) - ref_lse).max() < 1e-3
-    out16 = run(w, is_causal=causal)   # 16-bit row sums, Q pre-scaled
-    assert_close(out16, ref, w["q"].dtype, str(case) + " (no lse)")
+    with _pick_shape(kernel):
+        out, lse = run(w, is_causal=causal, return_lse=True)   # persistent 32-query, fp32 row sums
+        assert_close(out, ref, w["q"].dtype, str(case))
+        assert np.abs(to64(lse) - ref_lse).max() < 1e-3
+        out16 = run(w, is_causal=causal)   # Q pre-scaled; 64-query waves where they apply
+    assert_close(out16, ref, w["q"].dtype, f"{case} {kernel} (no lse)")
 
 
 def test_deterministic():
@@ -211,15 +214,14 @@ def _sampled_rows_causal(w, out, picks, rows):
             assert_close(out[b:b + 1, h:h + 1, i0:i1], ref, q.dtype, f"b{b} h{h} rows {i0}:{i1}")
 
 
-@pytest.mark.parametrize("qpw", [None, 64, 32])
-def test_causal_gqa_prefill_full_size_sampled(qpw, monkeypatch):
+@pytest.mark.parametrize("qpw", [None, "persistent", 64, 32])
+def test_causal_gqa_prefill_full_size_sampled(qpw):
     """B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal, in the benchmark's launch configuration
-    (qpw None) and with the one-item-per-group kernels (64- and 32-query waves); sampled rows
-    across the sequence checked against the oracle."""
-    if qpw is not None:
-        _pick_shape(monkeypatch, qpw)
+    (qpw None) and with the other kernels (persistent 32-query waves, one-item-per-group 64-
+    and 32-query waves); sampled rows across the sequence checked against the oracle."""
     w = causal_gqa_prefill()
-    out = run(w, is_causal=True)
+    with (_pick_shape(qpw) if qpw is not None else tune()):
+        out = run(w, is_causal=True)
     assert tuple(out.shape) == (4, 32, 4096, 128)
     assert torch.isfinite(out).all()
     _sampled_rows_causal(w, out.cpu(), [(0, 0), (1, 5), (2, 17), (3, 31)],
