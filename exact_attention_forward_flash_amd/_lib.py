@@ -12,6 +12,7 @@ WF_F32, WF_F16, WF_BF16, WF_BOOL, WF_I32 = 0, 1, 2, 3, 4
 STATUS = {0: "WF_OK", 1: "WF_ERR_NULL", 2: "WF_ERR_SHAPE", 3: "WF_ERR_DTYPE",
           4: "WF_ERR_LAYOUT", 5: "WF_ERR_UNSUPPORTED", 6: "WF_ERR_CHUNK_ORDER",
           7: "WF_ERR_CACHE_CONFIG", 8: "WF_ERR_WORKSPACE", 9: "WF_ERR_HIP"}
+ERR_SHAPE = 2
 ERR_CHUNK_ORDER = 6
 ERR_CACHE_CONFIG = 7
 

@@ -157,23 +157,37 @@ def varlen_mla_prefill_workspace_size(batch, total_q_tokens, head_num):
                                                                 int(head_num)))
 
 
+def _mla_kv(k, k_rope, v, kv_head_num, kv_layout):
+    if kv_layout == "padded":
+        return tuple(t if t.dim() == 4 else t.view(t.shape[0], t.shape[1], int(kv_head_num), -1)
+                     for t in (k, k_rope, v))
+    if kv_layout != "packed":
+        raise ValueError("kv_layout must be 'packed' or 'padded'")
+    return k, k_rope, v
+
+
 def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, kv_head_num,
-                       qk_scale, mask_type=1, workspace=None, kv_layout="packed"):
+                       qk_scale, mask_type=1, workspace=None, kv_layout="packed", check_lengths=None):
     """Varlen MLA prefill: q [nTq,Hq,128], q_rope [nTq,Hq,64], device int32 lengths [batch];
     mask_type 0 = none, 1 = causal (bottom-right). K/V come packed (kv_layout "packed":
     k/v [nTk,Hkv,128], k_rope [nTk,Hkv,64]) or padded per sequence (kv_layout "padded":
     k/v [batch,max_seq,Hkv*128] or [batch,max_seq,Hkv,128], k_rope likewise with 64).
-    Returns out [nTq, Hq, 128]."""
+    Returns out [nTq, Hq, 128].
+
+    The lengths live on the device, so the library checks them there: bad lengths (negative,
+    summing past nTq or nTk, longer than max_seq) compute nothing and set int32 word 2 of the
+    workspace to 1. With check_lengths (the default when no workspace is passed, since the
+    word would otherwise be lost with the temporary workspace) the call waits for the stream
+    and raises WfError on that word; with a caller's workspace and check_lengths False the
+    call stays asynchronous and the caller reads the word."""
     lib = _lib.load()
     batch = int(q_seqlen.numel())
-    if kv_layout == "padded":
-        k, k_rope, v = (t if t.dim() == 4 else t.view(t.shape[0], t.shape[1], int(kv_head_num), -1)
-                        for t in (k, k_rope, v))
-    elif kv_layout != "packed":
-        raise ValueError("kv_layout must be 'packed' or 'padded'")
+    k, k_rope, v = _mla_kv(k, k_rope, v, kv_head_num, kv_layout)
     n_q = q.shape[0]
     out = torch.empty((n_q, head_num, v.shape[-1]), dtype=q.dtype, device=q.device)
     need = varlen_mla_prefill_workspace_size(batch, n_q, head_num)
+    if check_lengths is None:
+        check_lengths = workspace is None
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     ds = [describe(t) for t in (q, q_rope, k, k_rope, v, out)]
@@ -183,6 +197,11 @@ def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, k
                                     int(kv_head_num), _scale(qk_scale), int(mask_type),
                                     _ref(ds[5]), ctypes.c_void_p(workspace.data_ptr()),
                                     workspace.numel(), _stream(q)))
+    if check_lengths and batch > 0 and n_q > 0:
+        if int(workspace[8:12].view(torch.int32).item()) != 0:     # .item() waits for the stream
+            raise _lib.WfError(_lib.ERR_SHAPE, "varlen_mla_prefill: device sequence lengths are "
+                               "negative, sum past the token counts or exceed max_seq; nothing "
+                               "was computed")
     return out
 
 

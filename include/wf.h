@@ -174,8 +174,14 @@ int wf_sdpa_decode(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, i
  *           aligned; it holds the tile schedule built on the device from the lengths.
  * Score width is Dv + 64 with Dv = 128 (the built instantiation).
  * If the device lengths are negative, sum past nTq (or, packed, nTk) or, padded, exceed
- * max_seq, no attention is computed and word 2 of the workspace (int32) is set to 1; it is 0
- * after a good call. A mix of packed and padded k / k_rope / v is WF_ERR_LAYOUT.
+ * max_seq, no attention is computed (out is left as it was) and word 2 of the workspace
+ * (int32) is set to 1; it is 0 after a good call. A mix of packed and padded k / k_rope / v
+ * is WF_ERR_LAYOUT.
+ * Where this differs from the two-phase interface the page defines: the workspace size is a
+ * function of (batch, nTq) rather than of the largest query length (the schedule is built
+ * on the device from the lengths, so the host never reads them and the bound must come from
+ * the token count; head_num is accepted and unused), the call itself takes no max_q_len for
+ * the same reason, and `stream` is a hipStream_t passed as void*.
  * ------------------------------------------------------------------------------------- */
 size_t wf_varlen_mla_prefill_workspace_size(int batch, int64_t total_q_tokens, int head_num);
 int wf_varlen_mla_prefill(const wf_tensor* q, const wf_tensor* q_rope, const wf_tensor* k,
@@ -247,9 +253,9 @@ const char* wf_last_error(void);
  * Process-wide values, initialised once from the environment variables WF_TUNE_<NAME>
  * (upper-case name) on first use, then changed only here; -1 restores the automatic choice.
  * Names: "hpw" (query heads per work group), "persist" (0: no persistent 32-query kernel),
- * "q64" (1: the persistent 64-query-wave kernel where it applies; off by default), "qpw" (32 | 64: queries per wave of the
- * one-item-per-group kernels), "nw" (4: waves per group of the 32-query kernel),
- * "decode_pack" (0: no (head, position) row packing in wf_sdpa_decode), "decode_groups",
+ * "q64" (1: the persistent 64-query-wave kernel where it applies; off by default),
+ * "qpw" (32 | 64: queries per wave of the one-item-per-group kernels), "nw" (4: waves per
+ * group of the 32-query kernel), "decode_pack" (0: no (head, position) row packing in wf_sdpa_decode), "decode_groups",
  * "decode_min_tiles" (split plan of wf_sdpa_decode), "mla_xcd" (0: no per-XCD split of the
  * MLA prefill), "attend_groups" (split plan of wf_block_kv_attend). Changing a value while
  * another thread launches work races with that launch's choice (never with its result's

@@ -144,6 +144,22 @@ def test_bad_lengths_set_the_error_word_and_compute_nothing():
     assert int(ws.view(torch.int32)[2]) == 0
 
 
+def test_bad_lengths_without_a_workspace_raise():
+    """With no workspace passed, the error word would go with the temporary workspace: the
+    binding waits and raises instead of returning an output nothing was written to."""
+    from exact_attention_forward_flash_amd import WfError
+    w = _inputs([100, 300], [100, 300], 2, 2, "bf16", seed=5)
+    t = {n: w[n].to(DEV) for n in ("q", "q_rope", "k", "k_rope", "v")}
+    bad = torch.tensor([100, 301], dtype=torch.int32, device=DEV)
+    with pytest.raises(WfError, match="lengths"):
+        varlen_mla_prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], bad, bad, 2, 2,
+                           w["qk_scale"], 1)
+    good = torch.tensor([100, 300], dtype=torch.int32, device=DEV)
+    out = varlen_mla_prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], good, good, 2, 2,
+                             w["qk_scale"], 1)
+    assert_close(out, _oracle(w), w["q"].dtype, "checked good call")
+
+
 def test_deterministic():
     w = _inputs([700, 50, 1300], [700, 50, 1300], 4, 4, "bf16", seed=6)
     assert torch.equal(_gpu(w), _gpu(w))
