@@ -50,6 +50,8 @@ SIGNATURES = {
     "wf_varlen_mla_prefill_workspace_size": (_sz, [_i32, _i64, _i32]),
     "wf_varlen_mla_prefill": (_i32, [_T, _T, _T, _T, _T, _vp, _vp, _i32, _i32, _i32, _f, _i32,
                                      _T, _vp, _sz, _vp]),
+    "wf_varlen_mla_prefill_noalloc": (_i32, [_T, _T, _T, _T, _T, _vp, _vp, _i32, _i32, _i32, _f,
+                                             _i32, _T, _vp]),
     "wf_block_kv_init": (_i32, [_S, _i64, _i64, _i64, _i64]),
     "wf_block_kv_cache_update": (_i32, [_S, _i64, _T, _T, _T, _T, _vp]),
     "wf_block_kv_visible": (_i32, [_S, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),

@@ -205,6 +205,24 @@ def varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, k
     return out
 
 
+def varlen_mla_prefill_noalloc(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, kv_head_num,
+                               qk_scale, out, mask_type=1, kv_layout="packed"):
+    """varlen_mla_prefill into a caller's `out` [nTq, Hq, 128] with the library's fixed 1 MiB
+    device workspace: nothing is allocated, so the call can sit in a HIP graph capture or a
+    serving loop that must not allocate. Calls on one device share that workspace and must
+    not overlap. Bad device lengths compute nothing and are not reported. Returns out."""
+    lib = _lib.load()
+    batch = int(q_seqlen.numel())
+    k, k_rope, v = _mla_kv(k, k_rope, v, kv_head_num, kv_layout)
+    ds = [describe(t) for t in (q, q_rope, k, k_rope, v, out)]
+    check(lib.wf_varlen_mla_prefill_noalloc(_ref(ds[0]), _ref(ds[1]), _ref(ds[2]), _ref(ds[3]),
+                                            _ref(ds[4]), ctypes.c_void_p(q_seqlen.data_ptr()),
+                                            ctypes.c_void_p(kv_seqlen.data_ptr()), batch,
+                                            int(head_num), int(kv_head_num), _scale(qk_scale),
+                                            int(mask_type), _ref(ds[5]), _stream(q)))
+    return out
+
+
 class BlockKVCache:
     """Rolling sink + window KV cache (WorldFoundry "Core 注意力", "Block KV cache 的调用顺序").
 

@@ -793,6 +793,71 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
   return hip_status(launch(e->fn, dim3(grid), dim3(e->nw * 64), a, s), "MLA launch");
 }
 
+}  // extern "C"
+
+// ---- scratch of wf_varlen_mla_prefill_noalloc ------------------------------------------
+// A fixed device array holds the prefill's workspace (schedule header, prefix sums, item list)
+// for callers that cannot allocate. Each device that runs the library has its own copy at its
+// own address, looked up once per device with that device current; host code uses only that
+// address (the array's name in host code is not a device address). Every call on a device
+// shares the array: the schedule kernel rewrites all of it that the attention kernel reads
+// (the counters, the item count and the error word included), so nothing needs clearing
+// between calls, and calls that overlap on one device race.
+static constexpr size_t kMlaScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) unsigned char scratch[kMlaScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(WF_ERR_UNSUPPORTED, "device %d: the static scratch covers devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+      if (p == nullptr) return fail(WF_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return WF_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int wf_varlen_mla_prefill_noalloc(const wf_tensor* q, const wf_tensor* q_rope, const wf_tensor* k,
+                                  const wf_tensor* k_rope, const wf_tensor* v,
+                                  const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
+                                  int head_num, int kv_head_num, float qk_scale, int mask_type,
+                                  wf_tensor* out, void* stream) {
+  if (q == nullptr) return fail(WF_ERR_NULL, "q is NULL");
+  // (a malformed q is rejected by the checks of wf_varlen_mla_prefill below)
+  const bool q_shaped = (q->ndim == 2 || q->ndim == 3) && q->shape[0] >= 0;
+  const size_t need = q_shaped ? wf_varlen_mla_prefill_workspace_size(batch, q->shape[0], head_num) : 0;
+  if (need > kMlaScratchBytes)
+    return fail(WF_ERR_WORKSPACE,
+                "the call needs %zu bytes of scratch and the static scratch holds %zu (batch %d, "
+                "%lld query tokens); use wf_varlen_mla_prefill with a workspace",
+                need, kMlaScratchBytes, batch, (long long)q->shape[0]);
+  void* ws = nullptr;
+  int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return wf_varlen_mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, batch, head_num,
+                               kv_head_num, qk_scale, mask_type, out, ws, kMlaScratchBytes, stream);
+}
+
 int wf_block_kv_init(wf_block_kv_state* s, int64_t cache_len, int64_t sink, int64_t window,
                      int64_t chunk) {
   if (s == nullptr) return fail(WF_ERR_NULL, "state is NULL");

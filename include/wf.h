@@ -191,6 +191,24 @@ int wf_varlen_mla_prefill(const wf_tensor* q, const wf_tensor* q_rope, const wf_
                           wf_tensor* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* wf_varlen_mla_prefill without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, layouts and results as wf_varlen_mla_prefill; the workspace
+ * is a fixed 1 MiB device array inside the library (one per device, held until the process
+ * ends). It serves any call whose wf_varlen_mla_prefill_workspace_size(batch, nTq, head_num)
+ * is at most 1 MiB: 8 bytes per work item (nTq / 256 + batch items) plus two (batch + 1)-entry
+ * offset tables, e.g. 1024 sequences with 30 million query tokens in all. A call that needs more returns WF_ERR_WORKSPACE and
+ * enqueues nothing. The call allocates nothing. All calls on one device share the array:
+ * calls that overlap on a device (two streams, or two threads) race and must be serialised
+ * by the caller; each call's schedule kernel rewrites everything the attention kernel reads,
+ * so consecutive calls need nothing cleared. Bad device lengths compute nothing, as above;
+ * the error word is then in the internal array and not visible to the caller. */
+int wf_varlen_mla_prefill_noalloc(const wf_tensor* q, const wf_tensor* q_rope, const wf_tensor* k,
+                                  const wf_tensor* k_rope, const wf_tensor* v,
+                                  const int32_t* q_seqlen, const int32_t* kv_seqlen, int batch,
+                                  int head_num, int kv_head_num, float qk_scale, int mask_type,
+                                  wf_tensor* out, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * Rolling block KV cache ([CORE] "Block KV cache 的调用顺序").
  *
