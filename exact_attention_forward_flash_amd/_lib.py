@@ -5,7 +5,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwf.so")
+# WF_LIBRARY names another build of the same sources (the host-sanitizer build, for one)
+LIB_PATH = os.environ.get("WF_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libwf.so")
 
 WF_F32, WF_F16, WF_BF16, WF_BOOL, WF_I32 = 0, 1, 2, 3, 4
 
@@ -62,22 +64,36 @@ SIGNATURES = {
     "wf_last_error": (ctypes.c_char_p, []),
     "wf_tune_set": (_i32, [ctypes.c_char_p, _i32]),
     "wf_tune_get": (_i32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int)]),
+    "wf_build_id": (ctypes.c_char_p, []),
 }
 
 _lib = None
 
 
+def check_build_id(lib_id, expected=None):
+    """Raises unless the library was built from the sources in this tree."""
+    from .build import source_hash
+    expected = expected or source_hash()
+    if lib_id != expected:
+        raise RuntimeError(f"{LIB_PATH} was built from other sources (build id {lib_id[:12]}, the "
+                           f"sources hash to {expected[:12]}); rebuild it with "
+                           "`python -m exact_attention_forward_flash_amd.build`")
+
+
 def load():
-    """Loads libwf.so once; raises if it has not been built."""
+    """Loads libwf.so once; raises if it has not been built or is older than the sources."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing; build it with "
                                "`python -m exact_attention_forward_flash_amd.build`")
         lib = ctypes.CDLL(LIB_PATH)
+        if not hasattr(lib, "wf_build_id"):
+            raise RuntimeError(f"{LIB_PATH} has no build id; rebuild it")
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype, fn.argtypes = res, args
+        check_build_id(lib.wf_build_id().decode())
         _lib = lib
     return _lib
 

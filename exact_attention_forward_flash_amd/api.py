@@ -268,6 +268,27 @@ class BlockKVCache:
             raise RuntimeError("after_update() index differs from before_update()")
         self._pending = None
 
+    def snapshot(self):
+        """A copy of the cache: the library state and both tensors (queued on k's stream)."""
+        if self._pending is not None:
+            raise RuntimeError("snapshot() between before_update() and after_update()")
+        st = WfBlockKvState()
+        ctypes.memmove(ctypes.byref(st), ctypes.byref(self.state), ctypes.sizeof(st))
+        return st, self.k.clone(), self.v.clone()
+
+    def restore(self, snap):
+        """Return the cache to a snapshot taken from a cache of the same shapes and sizes."""
+        st, k, v = snap
+        if tuple(k.shape) != self.k_shape or tuple(v.shape) != self.v_shape:
+            raise ValueError("snapshot shapes differ from this cache's")
+        if (st.cache_len, st.sink, st.window, st.chunk) != (self.state.cache_len, self.state.sink,
+                                                             self.state.window, self.state.chunk):
+            raise ValueError("snapshot sizes differ from this cache's")
+        self.k.copy_(k)
+        self.v.copy_(v)
+        ctypes.memmove(ctypes.byref(self.state), ctypes.byref(st), ctypes.sizeof(st))
+        self._pending = None
+
     def n_visible(self):
         """Number of visible cached tokens (the library's count, without the slot list)."""
         n = ctypes.c_int64()

@@ -266,6 +266,10 @@ int wf_block_kv_attend(const wf_block_kv_state* st, const wf_tensor* q,
 const char* wf_status_string(int status);
 const char* wf_last_error(void);
 
+/* Hex sha256 of the sources, headers and compile flags this library was built from (static
+ * string). The Python package compares it with the tree it sits in and refuses a stale build. */
+const char* wf_build_id(void);
+
 /* Kernel-selection overrides, for tests that must reach every kernel shape and for tuning
  * (not part of the pages' operation; every setting computes the same attention).
  * Process-wide values, initialised once from the environment variables WF_TUNE_<NAME>

@@ -251,3 +251,45 @@ def test_cache_slots_hold_the_oracles_visible_tokens(lib, sink, window, chunk):
         vis = _visible(lib, s)
         assert [slots[p] for p in vis] == o.cached_k()[0, 0, :, 0].tolist()
         idx = idx + 1 if rng.random() < 0.75 else idx
+
+
+def test_noalloc_prefill_rejects_before_touching_the_device(lib):
+    n, H = 100, 4
+    q, qr = T([n, H, 128]), T([n, H, 64])
+    k, kr, v, out = T([n, H, 128]), T([n, H, 64]), T([n, H, 128]), T([n, H, 128])
+
+    def call(q=q, batch=3):
+        return lib.wf_varlen_mla_prefill_noalloc(q if q is None else ctypes.byref(q),
+                                                 ctypes.byref(qr), ctypes.byref(k),
+                                                 ctypes.byref(kr), ctypes.byref(v), FAKE, FAKE,
+                                                 batch, H, H, 0.1, 1, ctypes.byref(out), None)
+    assert call(q=None) == NULL
+    many = 200_000                                   # 8 bytes of schedule per sequence: > 1 MiB
+    assert lib.wf_varlen_mla_prefill_workspace_size(many, n, H) > (1 << 20)
+    assert call(batch=many) == WS
+    assert "1048576" in lib.wf_last_error().decode()
+
+
+def test_library_build_id_matches_the_sources(lib):
+    from exact_attention_forward_flash_amd.build import source_hash
+    assert lib.wf_build_id().decode() == source_hash()
+    with pytest.raises(RuntimeError, match="rebuild"):
+        _lib.check_build_id("0" * 64)
+
+
+def test_source_hash_follows_every_source_and_header(tmp_path, monkeypatch):
+    import shutil
+    from exact_attention_forward_flash_amd import build as b
+    root = tmp_path / "tree"
+    shutil.copytree(b.CSRC, root / "pkg" / "csrc")
+    shutil.copytree(os.path.join(b.ROOT, "include"), root / "include")
+    monkeypatch.setattr(b, "ROOT", str(root))
+    monkeypatch.setattr(b, "CSRC", str(root / "pkg" / "csrc"))
+    base = b.source_hash()
+    for rel in ("pkg/csrc/attn_fwd_p.hpp", "pkg/csrc/wf_api.cpp", "include/wf.h"):
+        p = root / rel
+        text = p.read_bytes()
+        p.write_bytes(text + b"\n")
+        assert b.source_hash() != base, rel
+        p.write_bytes(text)
+        assert b.source_hash() == base

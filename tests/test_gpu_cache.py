@@ -135,3 +135,43 @@ def test_decode_over_the_cache_gqa():
             ref, _ = oracle.sdpa(q, kv, vv, scale=np.float32(1.0 / np.sqrt(128.0)))
             assert_close(out, ref, torch.float16, f"chunk {idx}")
         c.after_update(idx)
+
+
+def test_snapshot_restore_continues_bit_identically():
+    """A snapshot taken mid-stream (state plus both tensors) restored into a second cache: both
+    copies then take the same chunks, with a repeated chunk and the roll past the window, and
+    agree bit for bit in contents, visible slots and attend outputs; restoring the original
+    cache to the snapshot replays the same trajectory again."""
+    sink, window, chunk, H, D = 64, 448, 64, 2, 128
+    shape = (1, H, sink + window, D)
+    g = torch.Generator().manual_seed(21)
+    chunks = [(i, torch.randn(1, H, chunk, D, generator=g).half(),
+               torch.randn(1, H, chunk, D, generator=g).half(),
+               torch.randn(1, 2 * H, 96, D, generator=g).half()) for i in range(16)]
+    chunks.insert(12, (11,) + chunks[11][1:])          # repeat chunk 11 (overwrite)
+    a = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=torch.float16)
+
+    def step(c, item):
+        idx, k, v, q = item
+        c.before_update(idx)
+        c.update(k.to(DEV), v.to(DEV))
+        out = c.attend(q.to(DEV))
+        c.after_update(idx)
+        return out
+
+    for item in chunks[:6]:
+        step(a, item)
+    snap = a.snapshot()
+    b = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=torch.float16)
+    b.restore(snap)
+    assert b.visible() == a.visible() and b.last_chunk == a.last_chunk == 5
+    outs_a = [step(a, item) for item in chunks[6:]]
+    outs_b = [step(b, item) for item in chunks[6:]]
+    assert all(torch.equal(x, y) for x, y in zip(outs_a, outs_b))
+    assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v)
+    assert a.visible() == b.visible() and a.last_chunk == b.last_chunk == 15
+    a.restore(snap)
+    outs_r = [step(a, item) for item in chunks[6:]]
+    assert all(torch.equal(x, y) for x, y in zip(outs_r, outs_b))
+    assert torch.equal(a.k, b.k) and a.visible() == b.visible()
+    assert torch.isfinite(outs_b[-1].float()).all()

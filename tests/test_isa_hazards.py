@@ -7,7 +7,7 @@ import subprocess
 
 import pytest
 
-from tests.isa_hazards import check_asm
+from tests.isa_hazards import check_asm, compiler_source_war_pairs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -34,6 +34,26 @@ def test_checker_finds_planted_hazards():
     assert len(bad) == 3, bad   # cvt -> mfma, mfma -> accvgpr read, dot2c -> add
 
 
+def test_checker_separates_source_war_by_operand():
+    """A VALU write right after an MFMA: harmless to SrcA/SrcB, a hazard to a VGPR SrcC that is
+    not also the destination, and a result read (not this rule) when SrcC is the destination."""
+    asm = "\n".join([
+        "_Zwar:",
+        "\tv_mfma_f32_32x32x16_bf16 v[40:55], v[20:23], v[8:11], v[40:55]",
+        "\tv_mov_b32_e32 v20, 0",                                  # SrcA: fine
+        "\tv_mov_b32_e32 v9, 0",                                   # SrcB: fine
+        "\ts_nop 7",
+        "\ts_nop 7",
+        "\tv_mfma_f32_32x32x16_bf16 v[60:75], v[20:23], v[8:11], v[80:95]",
+        "\tv_mov_b32_e32 v81, 0",                                  # SrcC, not the destination
+        "\ts_nop 7",
+        "\ts_nop 7",
+        "\tv_mov_b32_e32 v82, 0",                                  # 17 wait states later: fine
+    ])
+    bad = check_asm(asm)["_Zwar"]
+    assert len(bad) == 1 and "v81" in bad[0], bad
+
+
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
 @pytest.mark.parametrize("src_name, kernel", [("sdpa_bf16_d128_w64.hip", "attn_fwd_w_kernel"),
@@ -44,8 +64,12 @@ def test_generated_code_has_no_inline_asm_hazards(tmp_path, src_name, kernel):
     out = tmp_path / "k.s"
     cmd = [HIPCC, *flags_for(src), "--cuda-device-only", "-S", src, "-o", str(out)]
     subprocess.run([c for c in cmd if c != "-fPIC"], check=True, capture_output=True)
-    res = check_asm(out.read_text())
+    text = out.read_text()
+    res = check_asm(text)
     kernels = [k for k in res if kernel in k]
     assert kernels, f"no {kernel} in the listing"
     for k in kernels:
         assert not res[k], (k, res[k][:5])
+    # the compiler's own schedule writes MFMA A/B registers in the very next instruction, which
+    # the inline asm relies on as well (no wait states for write-after-read of SrcA/SrcB)
+    assert compiler_source_war_pairs(text.splitlines()) > 0
