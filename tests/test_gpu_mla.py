@@ -6,7 +6,7 @@ import torch
 import oracle
 from exact_attention_forward_flash_amd import varlen_mla_prefill, varlen_mla_prefill_workspace_size
 from synth import varlen_mla_prefill_inputs
-from tests.parity import assert_close
+from tests.parity import assert_close, to64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -163,6 +163,42 @@ def test_bad_lengths_without_a_workspace_raise():
 def test_deterministic():
     w = _inputs([700, 50, 1300], [700, 50, 1300], 4, 4, "bf16", seed=6)
     assert torch.equal(_gpu(w), _gpu(w))
+
+
+@pytest.fixture(scope="module")
+def mla_full_call():
+    w = varlen_mla_prefill_inputs()
+    return w, _gpu(w).cpu()
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_varlen_mla_full_size_every_row(mla_full_call, part):
+    """Every output row of the full-size varlen MLA call (16 sequences, 16 heads) against the
+    oracle, sequences split over four parts by length rank so the parts cost about the same;
+    rows in blocks of 512, each a bottom-right causal problem over the keys up to its last row."""
+    w, out = mla_full_call
+    lens = w["q_seqlen"].tolist()
+    cu = oracle.cu_seqlens(lens)
+    order = [int(i) for i in np.argsort(lens)[::-1]]          # longest first, dealt in a snake
+    snake = [i % 4 if (i // 4) % 2 == 0 else 3 - i % 4 for i in range(len(order))]
+    mine = [si for si, p in zip(order, snake) if p == part]
+    errs = []
+    for si in mine:
+        L, base = lens[si], int(cu[si])
+        for i0 in range(0, L, 512):
+            i1 = min(L, i0 + 512)
+            rows, keys = slice(base + i0, base + i1), slice(base, base + i1)
+            ref = oracle.varlen_mla_prefill(
+                w["q"][rows], w["q_rope"][rows], w["k"][keys], w["k_rope"][keys], w["v"][keys],
+                [i1 - i0], [i1], 16, 16, np.float32(w["qk_scale"]), 1)
+            errs.append((np.abs(to64(out[rows]) - ref), f"seq {si} rows {i0}:{i1}"))
+    g = np.concatenate([e.reshape(-1) for e, _ in errs])
+    mx, mean = float(g.max()), float(g.mean())
+    worst = max(errs, key=lambda e: e[0].max())[1]
+    msg = f"sequences {mine}: max abs err {mx:.3g} (at {worst}), mean abs err {mean:.3g}"
+    assert np.isfinite(to64(out)).all()
+    assert mx <= 2e-2 and mean <= 2e-3, msg
+    print(msg)
 
 
 def test_varlen_mla_full_size_sampled():

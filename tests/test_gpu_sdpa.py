@@ -214,13 +214,43 @@ def _sampled_rows_causal(w, out, picks, rows):
             assert_close(out[b:b + 1, h:h + 1, i0:i1], ref, q.dtype, f"b{b} h{h} rows {i0}:{i1}")
 
 
-@pytest.mark.parametrize("qpw", [None, "persistent", 64, 32])
-def test_causal_gqa_prefill_full_size_sampled(qpw):
-    """B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal, in the benchmark's launch configuration
-    (qpw None) and with the other kernels (persistent 32-query waves, one-item-per-group 64-
-    and 32-query waves); sampled rows across the sequence checked against the oracle."""
+@pytest.fixture(scope="module")
+def gqa_4k_bench_call():
+    """The benchmark call (B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal, no lse, default
+    kernel choice) and its output on the host."""
     w = causal_gqa_prefill()
-    with (_pick_shape(qpw) if qpw is not None else tune()):
+    with tune():
+        out = run(w, is_causal=True)
+    return w, out.cpu()
+
+
+@pytest.mark.parametrize("b", range(4))
+def test_causal_gqa_prefill_full_size_every_row(gqa_4k_bench_call, b):
+    """Every output row of batch b of the benchmark call against the oracle (all 32 heads, all
+    4,096 rows; rows in blocks of 512, each block a bottom-right causal problem over the keys
+    up to its last row, which is the same definition restricted to the keys a row can see)."""
+    w, out = gqa_4k_bench_call
+    assert tuple(out.shape) == (4, 32, 4096, 128)
+    q, k, v = w["q"], w["k"], w["v"]
+    ref = np.empty((1, 32, 4096, 128))
+    for h in range(32):
+        for i0 in range(0, 4096, 512):
+            i1 = i0 + 512
+            ref[:, h:h + 1, i0:i1], _ = oracle.sdpa(
+                q[b:b + 1, h:h + 1, i0:i1], k[b:b + 1, h // 4:h // 4 + 1, :i1],
+                v[b:b + 1, h // 4:h // 4 + 1, :i1], is_causal=True,
+                scale=np.float32(w["scale"]), causal_align="bottom_right")
+    mx, mean = assert_close(out[b:b + 1], ref, torch.bfloat16, f"batch {b}, every row")
+    print(f"4k causal GQA batch {b}: max abs err {mx:.3g}, mean abs err {mean:.3g}")
+
+
+@pytest.mark.parametrize("qpw", ["persistent", 64, 32])
+def test_causal_gqa_prefill_full_size_sampled(qpw):
+    """B=4, Hq=32, Hkv=8, L=4096, d=128 bf16 causal with each kernel the dispatcher can pick
+    for it (persistent 32-query waves, one-item-per-group 64- and 32-query waves); sampled rows
+    across the sequence checked against the oracle."""
+    w = causal_gqa_prefill()
+    with _pick_shape(qpw):
         out = run(w, is_causal=True)
     assert tuple(out.shape) == (4, 32, 4096, 128)
     assert torch.isfinite(out).all()
