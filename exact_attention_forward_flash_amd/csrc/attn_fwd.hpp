@@ -91,7 +91,9 @@ __device__ __forceinline__ int lds_kswz(int row) {
 }
 template <int CH>
 __device__ __forceinline__ int lds_vswz(int row) {
-  return CH == 16 ? (((row & 1) * 6) ^ ((row & 2) * 5)) : 2 * (row & 3);
+  // 12-chunk (96-wide) rows: the swizzle stays inside aligned groups of 4 chunks, and the
+  // 4 rows of a transpose read (192 bytes apart) land on disjoint banks.
+  return CH == 16 ? (((row & 1) * 6) ^ ((row & 2) * 5)) : CH == 12 ? 2 * ((row >> 1) & 1) : 2 * (row & 3);
 }
 
 template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
@@ -106,7 +108,9 @@ struct AttnFwd {
   static constexpr int BMP = WPH * 32;
   static constexpr int NT = NW * 64;
   static constexpr int KLOADS = BN * KCH / NT;
-  static constexpr int VLOADS = BN * VCH / NT;
+  // V copies: whole waves of 64 chunks; with 96-wide rows the last round covers only part of
+  // the group (the waves past the tile skip it)
+  static constexpr int VLOADS = (BN * VCH + NT - 1) / NT;
   static constexpr int KBYTES = BN * DQK * 2;
   static constexpr int VBYTES = BN * DV * 2;
   static constexpr int NS = DQK / 16;
@@ -130,8 +134,9 @@ struct AttnFwd {
   static constexpr int KALIGN = (KBYTES == VBYTES && (KBYTES & (KBYTES - 1)) == 0) ? KBYTES : 1024;
   static_assert(sizeof(T) == 2, "16-bit inputs only");
   static_assert(NW % HPW == 0, "waves split evenly over heads");
-  static_assert((BN * KCH) % NT == 0 && (BN * VCH) % NT == 0, "tile copies split evenly");
-  static_assert(KCH % 8 == 0 && VCH % 8 == 0 && DQK1 % 16 == 0 && DV % 32 == 0, "tile shape");
+  static_assert((BN * KCH) % NT == 0 && (BN * VCH) % 64 == 0, "tile copies split evenly");
+  static_assert(KCH % 8 == 0 && (VCH % 8 == 0 || VCH == 12) && DQK1 % 16 == 0 && DV % 32 == 0,
+                "tile shape");
 
   static __device__ __forceinline__ int kswz(int row) { return lds_kswz<KCH>(row); }
   static __device__ __forceinline__ int vswz(int row) { return lds_vswz<VCH>(row); }
@@ -213,7 +218,8 @@ struct AttnFwd {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int p = (i * NW + w) * 64 + lane;
-      const int r = p / VCH, pos = p % VCH;
+      const int pc = p < BN * VCH ? p : BN * VCH - 1;   // past the tile: never issued
+      const int r = pc / VCH, pos = pc % VCH;
       vrow[i] = r;
       vsrc[i] = vp + ((pos ^ vswz(r)) * 8);
     }
@@ -233,6 +239,7 @@ struct AttnFwd {
       const int k0 = kt * BN;
 #pragma unroll
       for (int i = 0; i < VLOADS; ++i) {
+        if ((BN * VCH) % NT != 0 && (i * NW + w) * 64 >= BN * VCH) continue;  // wave-uniform
         int r = k0 + vrow[i];
         r = r < lk_last ? r : lk_last;
         dma16(vsrc[i] + (int64_t)r * a.v_sm, Vt + (i * NW + w) * 1024);

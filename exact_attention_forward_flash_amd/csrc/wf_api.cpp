@@ -147,6 +147,7 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
   typedef const wf::AttnEntry* (*TableFn)(int*);
   static const TableFn tables[] = {wf::attn_table_sdpa_bf16_d64, wf::attn_table_sdpa_bf16_d128,
                                    wf::attn_table_sdpa_f16_d64,  wf::attn_table_sdpa_f16_d128,
+                                   wf::attn_table_sdpa_bf16_dmix, wf::attn_table_sdpa_f16_dmix,
                                    wf::attn_table_mla,           wf::attn_table_split_bf16,
                                    wf::attn_table_split_f16,     wf::attn_table_splitp_bf16,
                                    wf::attn_table_splitp_f16,
@@ -514,7 +515,7 @@ int sdpa_validate(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
   if ((rc = resolve_scale(scale, Dqk, &plan->scale))) return rc;
   const bool f32 = q->dtype == WF_F32;
   if (f32 ? !((Dqk == 64 || Dqk == 128) && (Dv == 64 || Dv == 96 || Dv == 128))
-          : !((Dqk == 64 && Dv == 64) || (Dqk == 128 && Dv == 128)))
+          : !((Dqk == 64 && (Dv == 64 || Dv == 96)) || (Dqk == 128 && (Dv == 128 || Dv == 64))))
     return fail(WF_ERR_UNSUPPORTED, "head dims Dqk=%lld Dv=%lld are not built for this dtype",
                 (long long)Dqk, (long long)Dv);
   if (lse && reinterpret_cast<uintptr_t>(lse) % 4 != 0)

@@ -88,8 +88,8 @@ typedef struct {
  *        scaled, masked scores per query (-inf for a query that keeps no key).
  * GQA: query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of Hkv.
  * A query that keeps no key gets out = 0.
- * Built head dims: 16-bit q: (Dqk, Dv) in {(64,64), (128,128)}; fp32: Dqk in {64,128},
- * Dv in {64, 96, 128}. Others return WF_ERR_UNSUPPORTED.
+ * Built head dims: 16-bit q: (Dqk, Dv) in {(64,64), (64,96), (128,128), (128,64)}; fp32:
+ * Dqk in {64,128}, Dv in {64, 96, 128}. Others return WF_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------------- */
 int wf_sdpa_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
                 const wf_tensor* mask, int is_causal, float dropout_p, float scale,

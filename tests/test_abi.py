@@ -108,6 +108,10 @@ def test_decode_validation_errors(lib):
                 v=T([2, 2, 4096, 128], _lib.WF_F32)) == DTYPE
     assert call(k=T([2, 3, 4096, 128]), v=T([2, 3, 4096, 128])) == SHAPE   # 8 % 3 != 0
     assert call(q=T([2, 8, 1, 96]), k=T([2, 2, 64, 96]), v=T([2, 2, 64, 96])) == UNSUP
+    # a value width other than the key width: wf_sdpa_fwd takes it, the split kernels do not
+    q64, k64, v96 = T([2, 8, 1, 64]), T([2, 2, 64, 64]), T([2, 2, 64, 96])
+    assert lib.wf_sdpa_decode_workspace_size(ctypes.byref(q64), ctypes.byref(k64), ctypes.byref(v96), 0) == 0
+    assert call(q=q64, k=k64, v=v96, out=T([2, 8, 1, 96])) == UNSUP
     assert call(out=T([2, 8, 2, 128])) == SHAPE
     assert call(scale=0.0) == UNSUP
     assert call(q=T([0, 8, 1, 128]), k=T([0, 2, 4096, 128]), v=T([0, 2, 4096, 128])) == OK

@@ -57,6 +57,59 @@ def test_random_shapes(case):
     assert np.abs(to64(lse)[live] - ref_lse[live]).max() < 1e-3
 
 
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float16])
+def test_page_example_16bit(dt):
+    """The page's example (q/k width 64, v width 96) with its inputs rounded to 16 bits."""
+    w = page_example_fp32()
+    q, k, v = (w[n].to(dt) for n in ("q", "k", "v"))
+    ref, ref_lse = oracle.sdpa(q, k, v, scale=np.float32(w["scale"]))
+    out, lse = sdpa(q.to(DEV), k.to(DEV), v.to(DEV), scale=w["scale"], return_lse=True)
+    assert tuple(out.shape) == (2, 8, 32, 96)
+    assert_close(out, ref, dt, "page example, 16-bit")
+    assert np.abs(to64(lse) - ref_lse).max() < 1e-3
+    assert_close(sdpa(q.to(DEV), k.to(DEV), v.to(DEV), scale=w["scale"]), ref, dt, "no lse")
+
+
+MIX_CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, Dqk, Dv, causal, mask
+    ("bf16", 2, 8, 8, 32, 48, 64, 96, False, None),
+    ("fp16", 1, 8, 2, 300, 129, 64, 96, True, None),
+    ("bf16", 2, 4, 1, 65, 700, 64, 96, False, "bool"),
+    ("fp16", 1, 2, 2, 257, 257, 64, 96, False, "f32"),
+    ("bf16", 1, 16, 4, 513, 513, 128, 64, True, None),
+    ("fp16", 2, 6, 3, 129, 1000, 128, 64, False, None),
+    ("bf16", 1, 2, 1, 1, 300, 128, 64, False, "half"),
+    ("fp16", 3, 4, 4, 100, 0, 128, 64, False, None),
+]
+
+
+@pytest.mark.parametrize("case", MIX_CASES, ids=[str(c) for c in MIX_CASES])
+def test_value_width_differs_from_key_width(case):
+    dt, B, Hq, Hkv, Lq, Lk, Dqk, Dv, causal, mk = case
+    w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, Dqk, Dv, dt, seed=zlib.crc32(str(case).encode()) % 1000)
+    g = torch.Generator().manual_seed(3)
+    m = None
+    if mk == "bool":
+        m = torch.rand(B, 1, Lq, Lk, generator=g) < 0.85
+    elif mk is not None:
+        m = torch.randn(B, Hq, Lq, Lk, generator=g)
+        m[torch.rand(m.shape, generator=g) < 0.1] = -float("inf")
+        m = m.to(w["q"].dtype if mk == "half" else torch.float32)
+    ref, ref_lse = oracle.sdpa(w["q"], w["k"], w["v"], mask=m, is_causal=causal,
+                               scale=np.float32(w["scale"]))
+    for lse in (False, True):
+        res = sdpa(w["q"].to(DEV), w["k"].to(DEV), w["v"].to(DEV),
+                   attn_mask=None if m is None else m.to(DEV), is_causal=causal,
+                   scale=w["scale"], return_lse=lse)
+        out = res[0] if lse else res
+        assert tuple(out.shape) == (B, Hq, Lq, Dv)
+        assert_close(out, ref, w["q"].dtype, f"{case} lse={lse}")
+        if lse:
+            live = np.isfinite(ref_lse)
+            assert np.array_equal(np.isfinite(to64(res[1])), live)
+            if live.any():
+                assert np.abs(to64(res[1])[live] - ref_lse[live]).max() < 1e-3
+
+
 F32_CASES = [(2, 4, 2, 33, 50, 64, 96, False), (1, 4, 4, 130, 70, 128, 128, True),
              (2, 2, 1, 64, 64, 64, 64, True), (1, 2, 2, 5, 300, 128, 64, False)]
 

@@ -1,5 +1,6 @@
 """Seeded random sweep of wf_sdpa_fwd against the fp64 oracle across the dispatch matrix:
-dtype, batch, GQA factor, ragged lengths (including 1 and 0 keys), head dim, causal or not,
+dtype, batch, GQA factor, ragged lengths (including 1 and 0 keys), head dims (value width equal
+to or different from the key width), causal or not,
 bool / 16-bit / fp32 masks, with and without the lse, contiguous or [B, S, H, D]-strided
 inputs. Which kernel runs (persistent, 64-query or 32-query, masked or not) follows from these,
 so the sweep covers every routing decision of the dense entry point."""
@@ -31,8 +32,11 @@ def _case(i):
     mask = None if causal or r.random() < 0.4 else str(r.choice(["bool", "half", "f32"]))
     lse = bool(r.random() < 0.5)
     strided = bool(r.random() < 0.3)
-    return dict(dt=dt, B=B, Hkv=Hkv, G=G, D=D, Lq=Lq, Lk=Lk, causal=causal, mask=mask, lse=lse,
-                strided=strided, seed=i)
+    # value width: the key width, or (64 -> 96, 128 -> 64); drawn last, so the other fields of
+    # every case are as they were before this draw existed
+    Dv = D if r.random() < 0.7 else {64: 96, 128: 64}[D]
+    return dict(dt=dt, B=B, Hkv=Hkv, G=G, D=D, Dv=Dv, Lq=Lq, Lk=Lk, causal=causal, mask=mask,
+                lse=lse, strided=strided, seed=i)
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
@@ -44,7 +48,7 @@ def test_random_case(i):
     Hq = Hkv * G
     q = torch.randn(B, Hq, Lq, D, generator=g).to(dt)
     k = torch.randn(B, Hkv, Lk, D, generator=g).to(dt)
-    v = torch.randn(B, Hkv, Lk, D, generator=g).to(dt)
+    v = torch.randn(B, Hkv, Lk, c["Dv"], generator=g).to(dt)
     m = None
     if c["mask"] == "bool":
         m = torch.rand(B, 1, Lq, Lk, generator=g) < 0.85
