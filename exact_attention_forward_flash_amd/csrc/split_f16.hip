@@ -12,6 +12,9 @@ static const AttnEntry kTable[] = {
     E(64, 1, true),   E(64, 2, true),   E(64, 4, true),
     E(128, 1, false), E(128, 2, false), E(128, 4, false),
     E(128, 1, true),  E(128, 2, true),  E(128, 4, true),
+    // 8 waves (two per SIMD) on 256 query rows of one head: the block KV cache attend
+    WF_ATTN_ENTRY(_Float16, DT_F16, 64, 64, 64, 8, 1, MASK_NONE, false, MODE_SPLIT),
+    WF_ATTN_ENTRY(_Float16, DT_F16, 128, 128, 128, 8, 1, MASK_NONE, false, MODE_SPLIT),
 };
 #undef E
 // packed (query head, position) rows: the G*Lq queries of a KV head share one work item

@@ -111,10 +111,10 @@ int check_cache_data(const wf_tensor* t, const char* name, bool* unit16) {
 // Kernel-selection overrides for tests and tuning: WF_TUNE_<NAME> from the environment, read
 // once on first use, then changed only through wf_tune_set. -1 = automatic choice.
 enum TuneKey { T_HPW, T_PERSIST, T_Q64, T_QPW, T_NW, T_DECODE_PACK, T_DECODE_GROUPS,
-               T_DECODE_MIN_TILES, T_MLA_XCD, T_ATTEND_GROUPS, T_COUNT };
+               T_DECODE_MIN_TILES, T_MLA_XCD, T_ATTEND_GROUPS, T_ATTEND_NW, T_COUNT };
 const char* const kTuneNames[T_COUNT] = {"hpw", "persist", "q64", "qpw", "nw", "decode_pack",
                                          "decode_groups", "decode_min_tiles", "mla_xcd",
-                                         "attend_groups"};
+                                         "attend_groups", "attend_nw"};
 std::atomic<int>* tune_table() {
   static std::atomic<int> t[T_COUNT];
   static std::once_flag once;
@@ -148,7 +148,8 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
   static const TableFn tables[] = {wf::attn_table_sdpa_bf16_d64, wf::attn_table_sdpa_bf16_d128,
                                    wf::attn_table_sdpa_f16_d64,  wf::attn_table_sdpa_f16_d128,
                                    wf::attn_table_sdpa_bf16_dmix, wf::attn_table_sdpa_f16_dmix,
-                                   wf::attn_table_mla,           wf::attn_table_split_bf16,
+                                   wf::attn_table_mla,           wf::attn_table_mla_v64,
+                                   wf::attn_table_split_bf16,
                                    wf::attn_table_split_f16,     wf::attn_table_splitp_bf16,
                                    wf::attn_table_splitp_f16,
                                    wf::attn_table_w_bf16_d64,    wf::attn_table_w_bf16_d128,
@@ -658,7 +659,9 @@ int wf_sdpa_rope_fwd(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v,
 size_t wf_varlen_mla_prefill_workspace_size(int batch, int64_t total_q_tokens, int head_num) {
   (void)head_num;
   if (batch < 0 || total_q_tokens < 0) return 0;
-  const int64_t bmp = 256;  // query positions per work item of the built MLA kernel
+  // query positions per work item of the smallest-tile MLA kernel (four query heads of a KV
+  // head per work group: 64 rows); the call picks the kernel from kv_head_num, unknown here
+  const int64_t bmp = 64;
   const int64_t max_items = total_q_tokens / bmp + batch;
   return (size_t)wf::VarlenWs::bytes(batch, max_items);
 }
@@ -734,7 +737,8 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
     return fail(WF_ERR_SHAPE, "the rotary part must be 64 wide");
   if (k.shape[2] != Dv || v.shape[2] != Dv || out.shape[2] != Dv)
     return fail(WF_ERR_SHAPE, "q, k, v and out must share the value width");
-  if (Dv != 128) return fail(WF_ERR_UNSUPPORTED, "value width %lld is not built (128)", (long long)Dv);
+  if (Dv != 128 && Dv != 64)
+    return fail(WF_ERR_UNSUPPORTED, "value width %lld is not built (128, 64)", (long long)Dv);
   if (mask_type != 0 && mask_type != 1)
     return fail(WF_ERR_UNSUPPORTED, "mask_type must be 0 (none) or 1 (causal)");
   if (batch < 0) return fail(WF_ERR_SHAPE, "batch must be >= 0");
@@ -749,11 +753,14 @@ int wf_varlen_mla_prefill(const wf_tensor* q_, const wf_tensor* q_rope_, const w
     return fail(WF_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const wf::AttnEntry* e = find_attn(kernel_dtype(q.dtype), 192, 128, 128, 0, 0, wf::MASK_NONE,
-                                     mask_type, wf::MODE_VARLEN);
+  // The query heads of a KV head share each K/V tile (as in the dense kernels).
+  const int G = head_num / kv_head_num;
+  const int hpw = tuned_hpw(G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1, G);
+  const wf::AttnEntry* e = find_attn(kernel_dtype(q.dtype), (int)Dv + 64, (int)Dv, (int)Dv, 8, hpw,
+                                     wf::MASK_NONE, mask_type, wf::MODE_VARLEN);
   if (!e) return fail(WF_ERR_UNSUPPORTED, "MLA kernel not built for this dtype");
   if (batch == 0 || nTq == 0) return ok();
-  if (e->bmp != 256) return fail(WF_ERR_UNSUPPORTED, "internal: MLA tile height changed");
+  if (e->bmp < 64) return fail(WF_ERR_UNSUPPORTED, "internal: MLA tile height below the workspace's");
   const int max_items = (int)(nTq / e->bmp + batch);
   int* ws = (int*)workspace;
   hipStream_t s = (hipStream_t)stream;
@@ -996,7 +1003,8 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   // The query heads of a KV head share each K/V tile (as in wf_sdpa_decode).
   const int64_t G = Hq / Hkv;
   const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
-  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, 4, hpw, wf::MASK_NONE, 0, wf::MODE_SPLIT);
+  const int nw = (hpw == 1 && tune(T_ATTEND_NW) == 8) ? 8 : 4;
+  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, nw, hpw, wf::MASK_NONE, 0, wf::MODE_SPLIT);
   if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
   const int n_kt = (int)((n_vis + e->bn - 1) / e->bn);
   const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);

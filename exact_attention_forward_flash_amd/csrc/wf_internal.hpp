@@ -29,6 +29,7 @@ const AttnEntry* attn_table_sdpa_f16_d128(int* n);
 const AttnEntry* attn_table_sdpa_bf16_dmix(int* n);
 const AttnEntry* attn_table_sdpa_f16_dmix(int* n);
 const AttnEntry* attn_table_mla(int* n);
+const AttnEntry* attn_table_mla_v64(int* n);
 const AttnEntry* attn_table_p_rope_bf16(int* n);
 const AttnEntry* attn_table_p_rope_f16(int* n);
 const AttnEntry* attn_table_p_ropei_bf16(int* n);

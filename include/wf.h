@@ -172,7 +172,8 @@ int wf_sdpa_decode(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, i
  *   workspace  device memory of at least
  *           wf_varlen_mla_prefill_workspace_size(batch, nTq, head_num) bytes, 256-byte
  *           aligned; it holds the tile schedule built on the device from the lengths.
- * Score width is Dv + 64 with Dv = 128 (the built instantiation).
+ * Score width is Dv + 64, Dv in {128, 64} (the built instantiations). The query heads of a
+ * KV head share each K/V tile, four (or two) to a work group when Hq / Hkv allows.
  * If the device lengths are negative, sum past nTq (or, packed, nTk) or, padded, exceed
  * max_seq, no attention is computed (out is left as it was) and word 2 of the workspace
  * (int32) is set to 1; it is 0 after a good call. A mix of packed and padded k / k_rope / v
@@ -196,9 +197,9 @@ int wf_varlen_mla_prefill(const wf_tensor* q, const wf_tensor* q_rope, const wf_
  * allocation). Same arguments, layouts and results as wf_varlen_mla_prefill; the workspace
  * is a fixed 1 MiB device array inside the library (one per device, held until the process
  * ends). It serves any call whose wf_varlen_mla_prefill_workspace_size(batch, nTq, head_num)
- * is at most 1 MiB: 8 bytes per work item (nTq / 256 + batch items) plus two (batch + 1)-entry
- * offset tables, e.g. 1024 sequences with 30 million query tokens in all. A call that needs more returns WF_ERR_WORKSPACE and
- * enqueues nothing. The call allocates nothing. All calls on one device share the array:
+ * is at most 1 MiB: 8 bytes per work item (nTq / 64 + batch items) plus two (batch + 1)-entry
+ * offset tables, e.g. 1024 sequences with 8 million query tokens in all. A call that needs
+ * more returns WF_ERR_WORKSPACE and enqueues nothing. The call allocates nothing. All calls on one device share the array:
  * calls that overlap on a device (two streams, or two threads) race and must be serialised
  * by the caller; each call's schedule kernel rewrites everything the attention kernel reads,
  * so consecutive calls need nothing cleared. Bad device lengths compute nothing, as above;
@@ -279,7 +280,7 @@ const char* wf_build_id(void);
  * "qpw" (32 | 64: queries per wave of the one-item-per-group kernels), "nw" (4: waves per
  * group of the 32-query kernel), "decode_pack" (0: no (head, position) row packing in wf_sdpa_decode), "decode_groups",
  * "decode_min_tiles" (split plan of wf_sdpa_decode), "mla_xcd" (0: no per-XCD split of the
- * MLA prefill), "attend_groups" (split plan of wf_block_kv_attend). Changing a value while
+ * MLA prefill), "attend_groups", "attend_nw" (split plan of wf_block_kv_attend). Changing a value while
  * another thread launches work races with that launch's choice (never with its result's
  * correctness). Returns WF_ERR_UNSUPPORTED for an unknown name, WF_ERR_NULL for a NULL
  * value pointer. */

@@ -19,16 +19,16 @@ def _gpu(w, **kw):
                               w["mask_type"], **kw)
 
 
-def _inputs(qlens, kvlens, H, Hkv, dtype="bf16", seed=1, mask_type=1):
+def _inputs(qlens, kvlens, H, Hkv, dtype="bf16", seed=1, mask_type=1, dv=128):
     g = torch.Generator().manual_seed(seed)
     nq, nk = sum(qlens), sum(kvlens)
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
     r = lambda *s: torch.randn(*s, generator=g).to(dt)
-    return {"q": r(nq, H, 128), "q_rope": r(nq, H, 64), "k": r(nk, Hkv, 128),
-            "k_rope": r(nk, Hkv, 64), "v": r(nk, Hkv, 128),
+    return {"q": r(nq, H, dv), "q_rope": r(nq, H, 64), "k": r(nk, Hkv, dv),
+            "k_rope": r(nk, Hkv, 64), "v": r(nk, Hkv, dv),
             "q_seqlen": torch.tensor(qlens, dtype=torch.int32),
             "kv_seqlen": torch.tensor(kvlens, dtype=torch.int32),
-            "head_num": H, "kv_head_num": Hkv, "qk_scale": 1.0 / np.sqrt(192.0),
+            "head_num": H, "kv_head_num": Hkv, "qk_scale": 1.0 / np.sqrt(dv + 64.0),
             "mask_type": mask_type}
 
 
@@ -38,21 +38,45 @@ def _oracle(w):
                                      w["kv_head_num"], np.float32(w["qk_scale"]), w["mask_type"])
 
 
-CASES = [  # q lengths, kv lengths, H, Hkv, dtype, mask_type
-    ([1, 63, 64, 65, 300, 0, 777], None, 4, 4, "bf16", 1),
-    ([1, 63, 64, 65, 300, 0, 777], None, 4, 4, "bf16", 0),
-    ([200, 31, 513], [260, 31, 600], 4, 2, "bf16", 1),   # cached prefix: kv_len > q_len
-    ([257, 1000], None, 2, 1, "fp16", 1),
-    ([90, 5], [40, 5], 2, 2, "fp16", 1),                  # kv_len < q_len: early rows see nothing
+CASES = [  # q lengths, kv lengths, H, Hkv, dtype, mask_type, value width
+    ([1, 63, 64, 65, 300, 0, 777], None, 4, 4, "bf16", 1, 128),
+    ([1, 63, 64, 65, 300, 0, 777], None, 4, 4, "bf16", 0, 128),
+    ([200, 31, 513], [260, 31, 600], 4, 2, "bf16", 1, 128),   # cached prefix: kv_len > q_len
+    ([257, 1000], None, 2, 1, "fp16", 1, 128),
+    ([90, 5], [40, 5], 2, 2, "fp16", 1, 128),                  # kv_len < q_len: early rows see nothing
+    # four / two query heads of a KV head share each K/V tile
+    ([1, 63, 64, 65, 300, 0, 777], None, 8, 2, "bf16", 1, 128),
+    ([200, 31, 513], [260, 31, 600], 16, 4, "fp16", 1, 128),
+    ([129, 700], [129, 900], 6, 3, "bf16", 0, 128),
+    ([64, 1, 500], None, 16, 1, "bf16", 1, 128),
+    # value width 64 (score width 128)
+    ([1, 63, 64, 65, 300, 0, 777], None, 4, 4, "bf16", 1, 64),
+    ([200, 31, 513], [260, 31, 600], 8, 2, "fp16", 1, 64),
+    ([257, 1000], None, 6, 3, "bf16", 0, 64),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
 def test_varlen_small(case):
-    qlens, kvlens, H, Hkv, dt, mt = case
-    w = _inputs(qlens, kvlens or qlens, H, Hkv, dt, mask_type=mt)
+    qlens, kvlens, H, Hkv, dt, mt, dv = case
+    w = _inputs(qlens, kvlens or qlens, H, Hkv, dt, mask_type=mt, dv=dv)
     out = _gpu(w)
+    assert tuple(out.shape) == (sum(qlens), H, dv)
     assert_close(out, _oracle(w), w["q"].dtype, str(case))
+
+
+def test_head_groups_match_one_head_per_group():
+    """The kernel sharing K/V tiles among four query heads gives what the one-head-per-group
+    kernel gives (both against the oracle, and within a few output ulps of each other)."""
+    from exact_attention_forward_flash_amd import tune
+    w = _inputs([300, 1000, 77], [300, 1000, 77], 16, 4, "bf16", seed=9)
+    ref = _oracle(w)
+    shared = _gpu(w)
+    with tune(hpw=1):
+        single = _gpu(w)
+    assert_close(shared, ref, torch.bfloat16, "HPW 4")
+    assert_close(single, ref, torch.bfloat16, "HPW 1")
+    assert (shared.float() - single.float()).abs().max().item() < 2e-2
 
 
 def test_flat_layout_and_concatenated_cache():

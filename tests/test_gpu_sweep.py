@@ -117,13 +117,14 @@ def test_random_mla(i):
     kvlens = [q if r.random() < 0.5 else int(r.choice([0, 1, 70, 300, 800])) for q in qlens]
     mt = int(r.integers(0, 2))
     padded = bool(r.random() < 0.3)
+    dv = 128 if r.random() < 0.7 else 64   # drawn last: the other fields are as before
     g = torch.Generator().manual_seed(100 + i)
     nq, nk = sum(qlens), sum(kvlens)
-    q, qr = torch.randn(nq, H, 128, generator=g).to(dt), torch.randn(nq, H, 64, generator=g).to(dt)
-    k, kr = torch.randn(nk, Hkv, 128, generator=g).to(dt), torch.randn(nk, Hkv, 64, generator=g).to(dt)
-    v = torch.randn(nk, Hkv, 128, generator=g).to(dt)
+    q, qr = torch.randn(nq, H, dv, generator=g).to(dt), torch.randn(nq, H, 64, generator=g).to(dt)
+    k, kr = torch.randn(nk, Hkv, dv, generator=g).to(dt), torch.randn(nk, Hkv, 64, generator=g).to(dt)
+    v = torch.randn(nk, Hkv, dv, generator=g).to(dt)
     ql, kl = torch.tensor(qlens, dtype=torch.int32), torch.tensor(kvlens, dtype=torch.int32)
-    scale = 1 / np.sqrt(192.0)
+    scale = 1 / np.sqrt(dv + 64.0)
     ref = oracle.varlen_mla_prefill(q, qr, k, kr, v, ql, kl, H, Hkv, np.float32(scale), mt)
     if padded:   # the same tokens, [batch, max_seq, Hkv, d] with zero padding rows
         ms = max(max(kvlens), 1)
@@ -139,7 +140,8 @@ def test_random_mla(i):
         kd, krd, vd = k.to(DEV), kr.to(DEV), v.to(DEV)
     out = varlen_mla_prefill(q.to(DEV), qr.to(DEV), kd, krd, vd, ql.to(DEV), kl.to(DEV), H, Hkv,
                              scale, mt, kv_layout="padded" if padded else "packed")
-    assert_close(out, ref, dt, f"MLA case {i}: q {qlens} kv {kvlens} H={H}/{Hkv} mask={mt} padded={padded}")
+    assert_close(out, ref, dt, f"MLA case {i}: q {qlens} kv {kvlens} H={H}/{Hkv} dv={dv} mask={mt} "
+                               f"padded={padded}")
 
 
 # ---------------------------------------------------------------- RoPE ----------------------
