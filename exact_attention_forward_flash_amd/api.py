@@ -319,8 +319,9 @@ class BlockKVCache:
     def cached_v(self):
         return self._gather(self.v)
 
-    def attend(self, q, scale=None, workspace=None):
-        """Non-causal attention of q [B,Hq,Lq,D] over every visible cached token."""
+    def attend(self, q, scale=None, workspace=None, is_causal=False):
+        """Attention of q [B,Hq,Lq,D] over every visible cached token, in chronological order;
+        is_causal: the queries are the last Lq visible tokens (bottom-right causal)."""
         lib = _lib.load()
         kc, vc = self._bhsd(self.k), self._bhsd(self.v)
         B, Hq, Lq = q.shape[:3]
@@ -330,7 +331,8 @@ class BlockKVCache:
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
         check(lib.wf_block_kv_attend(ctypes.byref(self.state), _ref(describe(q)), _ref(describe(kc)),
-                                     _ref(describe(vc)), _scale(scale), _ref(describe(out)),
+                                     _ref(describe(vc)), 1 if is_causal else 0, _scale(scale),
+                                     _ref(describe(out)),
                                      ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                      _stream(q)))
         return out

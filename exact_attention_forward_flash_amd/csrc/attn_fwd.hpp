@@ -72,6 +72,9 @@ struct FwdArgs {
   // position); rotate-half kernels take rq_rot = head dim
   const float* rq_cos; const float* rq_sin;
   int rq_rot;
+  // block KV cache (split mode): key row t is the t-th visible token in chronological order,
+  // held in slot t (t < rm_head: the sink) or rm_sink + (rm_off + t - rm_head) mod rm_window
+  int kv_remap, rm_head, rm_sink, rm_off, rm_window;
 };
 
 struct WorkItem {
@@ -224,6 +227,14 @@ struct AttnFwd {
       vsrc[i] = vp + ((pos ^ vswz(r)) * 8);
     }
     const int lk_last = it.Lk - 1;
+    // Memory row of key row r: r itself, or (block KV cache) the slot of the r-th visible
+    // token, so that key rows run in chronological order whatever the ring's rotation.
+    auto key_row = [&](int r) {
+      if (MODE != MODE_SPLIT || !a.kv_remap || r < a.rm_head) return r;
+      int x = a.rm_off + (r - a.rm_head);   // < 2 * rm_window
+      x = x >= a.rm_window ? x - a.rm_window : x;
+      return a.rm_sink + x;
+    };
     // Rows past the last key are clamped onto it: their scores are masked to -inf, and
     // the duplicated V rows meet p = 0.
     auto issue_k = [&](int kt, WF_LDS char* Kt) {
@@ -231,7 +242,7 @@ struct AttnFwd {
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i) {
         int r = k0 + krow[i];
-        r = r < lk_last ? r : lk_last;
+        r = key_row(r < lk_last ? r : lk_last);
         dma16(ksrc[i] + (int64_t)r * kstride[i], Kt + (i * NW + w) * 1024);
       }
     };
@@ -241,7 +252,7 @@ struct AttnFwd {
       for (int i = 0; i < VLOADS; ++i) {
         if ((BN * VCH) % NT != 0 && (i * NW + w) * 64 >= BN * VCH) continue;  // wave-uniform
         int r = k0 + vrow[i];
-        r = r < lk_last ? r : lk_last;
+        r = key_row(r < lk_last ? r : lk_last);
         dma16(vsrc[i] + (int64_t)r * a.v_sm, Vt + (i * NW + w) * 1024);
       }
     };

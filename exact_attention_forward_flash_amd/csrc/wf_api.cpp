@@ -966,8 +966,8 @@ size_t wf_block_kv_attend_workspace_size(const wf_block_kv_state* s, int B, int 
 }
 
 int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_tensor* k_cache,
-                       const wf_tensor* v_cache, float scale, wf_tensor* out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       const wf_tensor* v_cache, int is_causal, float scale, wf_tensor* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   int rc;
   if ((rc = check_cache_state(s))) return rc;
   if ((rc = check_data(q, "q", 4)) || (rc = check_data(k_cache, "k_cache", 4)) ||
@@ -994,17 +994,19 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if (B * Hq * Lq == 0) return ok();
+  if (s->cache_len > 0x7fffffff) return fail(WF_ERR_SHAPE, "cache_len exceeds 2^31");
   int64_t T, head, start, n_vis;
   visible_range(s, &T, &head, &start, &n_vis);
-  // Every visible token sits in a slot below n_vis (tokens before the window wraps keep
-  // slot == token; once it wraps every slot is visible), and a non-causal softmax over keys
-  // does not depend on their order, so the kernels read slots [0, n_vis) in place.
+  // The split kernel reads the visible tokens in chronological order through the slot map
+  // (sink prefix, then the window from its oldest token, wrapping round the ring).
   const int dt = kernel_dtype(q->dtype);
   // The query heads of a KV head share each K/V tile (as in wf_sdpa_decode).
   const int64_t G = Hq / Hkv;
   const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
-  const int nw = (hpw == 1 && tune(T_ATTEND_NW) == 8) ? 8 : 4;
-  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, nw, hpw, wf::MASK_NONE, 0, wf::MODE_SPLIT);
+  const int causal = is_causal ? 1 : 0;
+  const int nw = (hpw == 1 && !causal && tune(T_ATTEND_NW) == 8) ? 8 : 4;
+  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, nw, hpw, wf::MASK_NONE, causal,
+                                     wf::MODE_SPLIT);
   if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
   const int n_kt = (int)((n_vis + e->bn - 1) / e->bn);
   const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
@@ -1019,11 +1021,14 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   int n_splits = (int)((target + base_blocks - 1) / base_blocks);
   if (n_splits > kMaxSplits) n_splits = kMaxSplits;
   if (n_splits > n_kt) n_splits = n_kt;
-  if (n_splits <= 1)
+  // One split suffices when the query tiles alone fill the GPU: a non-causal attend does
+  // not depend on the order of the keys, so the dense kernels read slots [0, n_vis) in place.
+  if (n_splits <= 1 && !causal && n_vis > 0)
     return run_dense(q, k_cache, v_cache, nullptr, wf::MASK_NONE, false, false, 0, sc, out, nullptr,
                      n_vis, (hipStream_t)stream);
-  const int tps = (n_kt + n_splits - 1) / n_splits;
-  n_splits = (n_kt + tps - 1) / tps;
+  if (n_splits < 1) n_splits = 1;
+  const int tps = n_kt > 0 ? (n_kt + n_splits - 1) / n_splits : 1;
+  n_splits = n_kt > 0 ? (n_kt + tps - 1) / tps : 1;
   wf::FwdArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = q->data; a.q2 = q->data; a.k = k_cache->data; a.k2 = k_cache->data; a.v = v_cache->data;
@@ -1039,6 +1044,14 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   a.scale_log2 = sc * wf::kLog2e;
   a.inv_scale = 1.0f / sc;
   a.tiles_per_split = tps;
+  // the chunk's queries are the last Lq visible tokens (bottom-right)
+  a.causal_shift = causal ? (int)(n_vis - Lq) : 0;
+  // key rows in chronological order: sink tokens, then the window from its oldest token
+  a.kv_remap = 1;
+  a.rm_head = (int)head;
+  a.rm_sink = (int)s->sink;
+  a.rm_off = (int)((start - s->sink) % s->window);
+  a.rm_window = (int)s->window;
   const int64_t rows = B * Hq * Lq;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + (size_t)kMaxSplits * rows * Dv * 4);

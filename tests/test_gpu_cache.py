@@ -175,3 +175,38 @@ def test_snapshot_restore_continues_bit_identically():
     assert all(torch.equal(x, y) for x, y in zip(outs_r, outs_b))
     assert torch.equal(a.k, b.k) and a.visible() == b.visible()
     assert torch.isfinite(outs_b[-1].float()).all()
+
+
+@pytest.mark.parametrize("sink,window,chunk,H,Hkv,dt", [
+    (64, 448, 64, 2, 2, torch.float16), (0, 256, 64, 4, 1, torch.bfloat16),
+    (32, 96, 32, 8, 2, torch.float16), (256, 3840, 256, 4, 4, torch.float16)])
+def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H, Hkv, dt):
+    """Causal attend (the chunk's queries are the newest visible tokens) across the roll of
+    the window: only a kernel that reads the ring in chronological order matches the oracle's
+    causal attention over its token list once the ring has wrapped; the non-causal attend
+    of the same chunk is checked too, and a single new query as in decoding."""
+    D = 64 if chunk < 256 else 128
+    shape = (1, Hkv, sink + window, D)
+    c = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=dt)
+    o = oracle.BlockKVCacheOracle(shape, shape, 2, chunk, window, sink)
+    g = torch.Generator().manual_seed(sink + window + chunk + H)
+    steps = (sink + window) // chunk + 5 if chunk < 256 else 18
+    for idx in range(steps):
+        k = torch.randn(1, Hkv, chunk, D, generator=g).to(dt)
+        v = torch.randn(1, Hkv, chunk, D, generator=g).to(dt)
+        q = torch.randn(1, H, chunk, D, generator=g).to(dt)
+        c.before_update(idx)
+        c.update(k.to(DEV), v.to(DEV))
+        o.update(idx, k.float().numpy(), v.float().numpy())
+        if idx % 3 == 2 or idx == steps - 1:
+            kv = torch.from_numpy(o.cached_k()).to(dt)
+            vv = torch.from_numpy(o.cached_v()).to(dt)
+            sc = np.float32(1.0 / np.sqrt(D))
+            ref, _ = oracle.sdpa(q, kv, vv, is_causal=True, scale=sc, causal_align="bottom_right")
+            assert_close(c.attend(q.to(DEV), is_causal=True), ref, dt, f"causal, chunk {idx}")
+            ref, _ = oracle.sdpa(q, kv, vv, scale=sc)
+            assert_close(c.attend(q.to(DEV)), ref, dt, f"non-causal, chunk {idx}")
+            q1 = q[:, :, -1:].contiguous()
+            ref, _ = oracle.sdpa(q1, kv, vv, is_causal=True, scale=sc, causal_align="bottom_right")
+            assert_close(c.attend(q1.to(DEV), is_causal=True), ref, dt, f"one query, chunk {idx}")
+        c.after_update(idx)
