@@ -10,8 +10,8 @@ namespace wf {
 //   cu_q, cu_k = exclusive prefix sums of the lengths ([batch + 1]);
 //   max_kv >= 0: keys and values are padded per sequence (max_kv rows each), so a sequence's
 //   kv length may not exceed max_kv and the packed total is not checked;
-//   one work item per (sequence, query tile of bmp positions), ordered by descending
-//   number of key tiles (longest first, so persistent work groups finish together).
+//   one work item per (sequence, query tile of bmp positions), sequence by sequence (longest
+//   sequences first, each sequence's tiles from its last query tile down).
 // One work group of 1024 threads; the attention kernel that follows on the stream takes
 // items from the counter this kernel resets.
 // ------------------------------------------------------------------------------------------
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
   __shared__ int64_t sm64[kSchedThreads];  // length sums: 1024 int32 lengths can overflow 32 bits
   __shared__ int hist[kSchedBuckets];
   __shared__ int s_bad;
+  (void)causal;   // the order does not depend on the mask: a sequence's last tile is its longest
   int* cu_q = (int*)((char*)ws + VarlenWs::cu_q_off());
   int* cu_k = (int*)((char*)ws + VarlenWs::cu_k_off(batch));
   int2* items = (int2*)((char*)ws + VarlenWs::items_off(batch));
@@ -91,9 +92,14 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
   const int bad = s_bad;
   const int n_pairs = bad ? 0 : (int)carry_items;
 
-  // Counting sort of the (sequence, query tile) items by descending key-tile count. Pass 0
-  // builds the histogram, then its exclusive scan turns counts into slot offsets; pass 1
-  // places the items. One thread walks the tiles of one sequence.
+  // Item order: sequence by sequence, sequences by descending key-tile count (a counting
+  // sort over buckets of that count, each sequence taking a contiguous run of slots), and
+  // within a sequence its query tiles from the last (most keys under the causal rule) to
+  // the first. Work groups that take consecutive items then stream the same sequence's K/V
+  // tiles at about the same time, so each tile is fetched once into L2 and read by many;
+  // the list still ends with the shortest items. Pass 0 adds each sequence's tile count to
+  // its bucket, the exclusive scan turns the sums into slot offsets, pass 1 claims a run of
+  // slots per sequence. One thread walks the tiles of one sequence.
   if (!bad) {
     for (int pass = 0; pass < 2; ++pass) {
       for (int base = 0; base < batch; base += kSchedThreads) {
@@ -103,25 +109,20 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
           const int lk = cu_k[bi + 1] - cu_k[bi];
           const int ntile = (int)(((int64_t)lq + bmp - 1) / bmp);
           const int n_kt = (int)(((int64_t)lk + bn - 1) / bn);
-          for (int tt = 0; tt < ntile; ++tt) {
-            int cost = n_kt;
-            if (causal) {
-              const int64_t lim = (int64_t)tt * bmp + bmp - 1 + ((int64_t)lk - lq);
-              cost = lim < 0 ? 0 : (lim / bn + 1 < n_kt ? (int)(lim / bn + 1) : n_kt);
-            }
-            const int bucket =
-                kSchedBuckets - 1 - (cost < kSchedBuckets - 1 ? cost : kSchedBuckets - 1);
+          const int bucket =
+              kSchedBuckets - 1 - (n_kt < kSchedBuckets - 1 ? n_kt : kSchedBuckets - 1);
+          if (ntile > 0) {
             if (pass == 0) {
-              atomicAdd(&hist[bucket], 1);
+              atomicAdd(&hist[bucket], ntile);
             } else {
-              const int pos = atomicAdd(&hist[bucket], 1);
-              items[pos] = make_int2(bi, tt);
+              const int pos = atomicAdd(&hist[bucket], ntile);
+              for (int j = 0; j < ntile; ++j) items[pos + j] = make_int2(bi, ntile - 1 - j);
             }
           }
         }
       }
       __syncthreads();
-      if (pass == 0) {  // exclusive scan of the histogram; bucket 0 holds the longest items
+      if (pass == 0) {  // exclusive scan of the histogram; bucket 0 holds the longest sequences
         int run = 0;
         for (int base = 0; base < kSchedBuckets; base += kSchedThreads) {
           int tot;
