@@ -111,10 +111,11 @@ int check_cache_data(const wf_tensor* t, const char* name, bool* unit16) {
 // Kernel-selection overrides for tests and tuning: WF_TUNE_<NAME> from the environment, read
 // once on first use, then changed only through wf_tune_set. -1 = automatic choice.
 enum TuneKey { T_HPW, T_PERSIST, T_Q64, T_QPW, T_NW, T_DECODE_PACK, T_DECODE_GROUPS,
-               T_DECODE_MIN_TILES, T_MLA_XCD, T_ATTEND_GROUPS, T_ATTEND_NW, T_COUNT };
+               T_DECODE_MIN_TILES, T_MLA_XCD, T_ATTEND_GROUPS, T_ATTEND_NW, T_ATTEND_MIN_TILES,
+               T_COUNT };
 const char* const kTuneNames[T_COUNT] = {"hpw", "persist", "q64", "qpw", "nw", "decode_pack",
                                          "decode_groups", "decode_min_tiles", "mla_xcd",
-                                         "attend_groups", "attend_nw"};
+                                         "attend_groups", "attend_nw", "attend_min_tiles"};
 std::atomic<int>* tune_table() {
   static std::atomic<int> t[T_COUNT];
   static std::once_flag once;
@@ -1021,6 +1022,13 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   int n_splits = (int)((target + base_blocks - 1) / base_blocks);
   if (n_splits > kMaxSplits) n_splits = kMaxSplits;
   if (n_splits > n_kt) n_splits = n_kt;
+  {
+    // each split keeps at least min_tiles key tiles: a split re-reads the queries and writes
+    // an fp32 partial row per query, which short key ranges do not pay for
+    const int min_tiles = tune(T_ATTEND_MIN_TILES) > 0 ? tune(T_ATTEND_MIN_TILES) : 1;
+    const int cap = std::max(1, n_kt / min_tiles);
+    if (n_splits > cap) n_splits = cap;
+  }
   // One split suffices when the query tiles alone fill the GPU: a non-causal attend does
   // not depend on the order of the keys, so the dense kernels read slots [0, n_vis) in place.
   if (n_splits <= 1 && !causal && n_vis > 0)
