@@ -29,6 +29,10 @@ CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, rot, style, q_pos0, k_pos0, causal
     ("fp16", 1, 2, 1, 33, 1000, 64, 32, 1, 0, 0, False),
     ("fp32", 2, 4, 2, 40, 70, 64, 48, 0, 3, 0, False),
     ("bf16", 1, 8, 8, 300, 300, 128, 0, 0, 0, 0, True),      # rot 0: plain attention
+    # interleaved pairs over half the head, causal GQA with four query heads per KV head
+    # (the persistent kernel turns Q as it reads it)
+    ("bf16", 2, 8, 2, 200, 200, 128, 64, 1, 0, 0, True),
+    ("fp16", 1, 16, 4, 257, 257, 128, 64, 1, 7, 7, True),
 ]
 
 
@@ -52,13 +56,35 @@ def test_rope_shapes(case):
     assert np.abs(to64(lse)[live] - ref_lse[live]).max() < tol
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[1]], ids=["rotate-half", "interleaved"])
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[6], CASES[7]],
+                         ids=["rotate-half", "interleaved", "interleaved-gqa4-bf16", "interleaved-gqa4-fp16"])
 def test_rope_separate_pass_path(case):
     """These cases (rotate-half over the whole head, causal GQA; interleaved over half the
-    head) turn Q in the persistent kernel's registers; with that kernel turned off their Q goes
-    through the separate pass instead, and both paths meet the bounds."""
+    head, also causal with four query heads per KV head) turn Q in the persistent kernel's
+    registers; with that kernel turned off their Q goes through the separate pass instead, and
+    both paths meet the bounds."""
     with tune(persist=0):
         test_rope_shapes(case)
+
+
+@pytest.mark.parametrize("case", [CASES[6], CASES[7]], ids=["bf16", "fp16"])
+def test_rope_interleaved_gqa_without_lse(case):
+    """Without the lse the persistent kernel takes its prescaled-Q variant, which turns Q and
+    then multiplies it by scale*log2(e); its output matches the oracle and the separate-pass
+    path (persistent kernel off) within the bounds."""
+    dt, B, Hq, Hkv, Lq, Lk, D, rot, style, qp, kp, causal = case
+    w = random_sdpa_inputs(B, Hq, Hkv, Lq, Lk, D, D, dt, seed=zlib.crc32(str(case).encode()) % 1000)
+    c, s = _tables(max(qp + Lq, kp + Lk) + 3, rot)
+    ref, _ = oracle.sdpa_rope(w["q"], w["k"], w["v"], c.double(), s.double(), rot, style, qp, kp,
+                              is_causal=causal, scale=np.float32(w["scale"]))
+    q, k, v = (w[n].to(DEV) for n in ("q", "k", "v"))
+    run = lambda: sdpa_rope(q, k, v, c.to(DEV), s.to(DEV), rot, style, qp, kp, is_causal=causal,
+                            scale=w["scale"])
+    fused = run()
+    with tune(persist=0):
+        separate = run()
+    assert_close(fused, ref, w["q"].dtype, f"{case} fused")
+    assert_close(separate, ref, w["q"].dtype, f"{case} separate pass")
 
 
 @pytest.mark.parametrize("tab_std,lse", [(1.0, True), (0.5 ** 0.5, False)], ids=["N(0,1)+lse", "N(0,1/2)"])
