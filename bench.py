@@ -233,6 +233,30 @@ def other_workload(name, steps, warmup):
                     update_gbs=round(upd_bytes * reps / (tot_u * 1e-3) / 1e9, 1),
                     attend_ms_per_chunk=round(tot_a / reps / n, 4),
                     attend_tflops=round(fl / (tot_a * 1e-3) / 1e12, 2))
+
+        # the same stream through the fused update + attend (one attention launch per chunk)
+        def run_fused(evs):
+            cache = wf.BlockKVCache((B, H, sink + window, D), (B, H, sink + window, D), 2, C,
+                                    window, sink, device=dev)
+            for i, (c, q, k, v) in enumerate(chunks):
+                e = ev_pool[i]
+                cache.before_update(c)
+                e[0].record(stream)
+                cache.update_attend(k, v, q, workspace=ws)
+                e[1].record(stream)
+                cache.after_update(c)
+                evs.append(e)
+
+        run_fused([])
+        torch.cuda.synchronize()
+        tot_f = 0.0
+        for _ in range(reps):
+            evs = []
+            run_fused(evs)
+            torch.cuda.synchronize()
+            tot_f += sum(e[0].elapsed_time(e[1]) for e in evs)
+        line.update(fused_update_attend_ms_per_chunk=round(tot_f / reps / n, 4),
+                    separate_update_plus_attend_ms_per_chunk=round((tot_u + tot_a) / reps / n, 4))
     elif name == "rope_gqa":
         import numpy as np
         w = synth.causal_gqa_prefill()

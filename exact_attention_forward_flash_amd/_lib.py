@@ -60,6 +60,7 @@ SIGNATURES = {
     "wf_block_kv_gather": (_i32, [_S, _T, _T, _vp]),
     "wf_block_kv_attend_workspace_size": (_sz, [_S, _i32, _i32, _i32, _i32]),
     "wf_block_kv_attend": (_i32, [_S, _T, _T, _T, _i32, _f, _T, _vp, _sz, _vp]),
+    "wf_block_kv_update_attend": (_i32, [_S, _i64, _T, _T, _T, _T, _T, _i32, _f, _T, _vp, _sz, _vp]),
     "wf_status_string": (ctypes.c_char_p, [_i32]),
     "wf_last_error": (ctypes.c_char_p, []),
     "wf_tune_set": (_i32, [ctypes.c_char_p, _i32]),

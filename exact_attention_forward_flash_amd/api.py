@@ -319,6 +319,26 @@ class BlockKVCache:
     def cached_v(self):
         return self._gather(self.v)
 
+    def update_attend(self, k, v, q, scale=None, workspace=None, is_causal=False):
+        """update(k, v) then attend(q) in one attention launch (between before_update and
+        after_update, like update); returns the attend's output."""
+        if self._pending is None:
+            raise RuntimeError("update_attend() without before_update()")
+        lib = _lib.load()
+        kc, vc = self._bhsd(self.k), self._bhsd(self.v)
+        B, Hq, Lq = q.shape[:3]
+        out = torch.empty((B, Hq, Lq, vc.shape[3]), dtype=q.dtype, device=q.device)
+        need = int(lib.wf_block_kv_attend_workspace_size(ctypes.byref(self.state), B, Hq, Lq,
+                                                         vc.shape[3]))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        check(lib.wf_block_kv_update_attend(
+            ctypes.byref(self.state), self._pending, _ref(describe(self._bhsd(k))),
+            _ref(describe(self._bhsd(v))), _ref(describe(kc)), _ref(describe(vc)), _ref(describe(q)),
+            1 if is_causal else 0, _scale(scale), _ref(describe(out)),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(q)))
+        return out
+
     def attend(self, q, scale=None, workspace=None, is_causal=False):
         """Attention of q [B,Hq,Lq,D] over every visible cached token, in chronological order;
         is_causal: the queries are the last Lq visible tokens (bottom-right causal)."""

@@ -75,6 +75,13 @@ struct FwdArgs {
   // block KV cache (split mode): key row t is the t-th visible token in chronological order,
   // held in slot t (t < rm_head: the sink) or rm_sink + (rm_off + t - rm_head) mod rm_window
   int kv_remap, rm_head, rm_sink, rm_off, rm_window;
+  // fused cache update (split mode): the chunk's new K / V rows [B, Hkv, upd_chunk, d] are
+  // read for key rows >= new_lo straight from knew / vnew, and the work groups also copy
+  // them into their ring slots (tokens upd_tok0 ..) of the caches a.k / a.v
+  int kv_new, new_lo, upd_chunk;
+  const void* knew; const void* vnew;
+  int64_t kn_sb, kn_sh, kn_sm, vn_sb, vn_sh, vn_sm;
+  int64_t upd_tok0;
 };
 
 struct WorkItem {
@@ -101,6 +108,8 @@ __device__ __forceinline__ int lds_vswz(int row) {
 
 template <typename T, int DQK, int DQK1, int DV, int NW, int HPW, int MASK, bool CAUSAL, int MODE>
 struct AttnFwd {
+  typedef T elem_t;
+  static constexpr int kDQK = DQK, kDV = DV;
   static constexpr int BN = 64;
   static constexpr int kNW = NW;
   static constexpr int kHPW = HPW;
@@ -237,13 +246,21 @@ struct AttnFwd {
     };
     // Rows past the last key are clamped onto it: their scores are masked to -inf, and
     // the duplicated V rows meet p = 0.
+    // Fused cache update: rows of the new chunk come from its own tensors (same bits as the
+    // slots the update writes, which this launch does not read).
+    const bool fresh = MODE == MODE_SPLIT && a.kv_new;
+    const T* knb = fresh ? (const T*)a.knew + it.b * a.kn_sb + g * a.kn_sh : nullptr;
+    const T* vnb = fresh ? (const T*)a.vnew + it.b * a.vn_sb + g * a.vn_sh : nullptr;
     auto issue_k = [&](int kt, WF_LDS char* Kt) {
       const int k0 = kt * BN;
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i) {
         int r = k0 + krow[i];
-        r = key_row(r < lk_last ? r : lk_last);
-        dma16(ksrc[i] + (int64_t)r * kstride[i], Kt + (i * NW + w) * 1024);
+        r = r < lk_last ? r : lk_last;
+        const T* src = (fresh && r >= a.new_lo)
+                           ? knb + (ksrc[i] - kp) + (int64_t)(r - a.new_lo) * a.kn_sm
+                           : ksrc[i] + (int64_t)key_row(r) * kstride[i];
+        dma16(src, Kt + (i * NW + w) * 1024);
       }
     };
     auto issue_v = [&](int kt, WF_LDS char* Vt) {
@@ -252,8 +269,11 @@ struct AttnFwd {
       for (int i = 0; i < VLOADS; ++i) {
         if ((BN * VCH) % NT != 0 && (i * NW + w) * 64 >= BN * VCH) continue;  // wave-uniform
         int r = k0 + vrow[i];
-        r = key_row(r < lk_last ? r : lk_last);
-        dma16(vsrc[i] + (int64_t)r * a.v_sm, Vt + (i * NW + w) * 1024);
+        r = r < lk_last ? r : lk_last;
+        const T* src = (fresh && r >= a.new_lo)
+                           ? vnb + (vsrc[i] - vp) + (int64_t)(r - a.new_lo) * a.vn_sm
+                           : vsrc[i] + (int64_t)key_row(r) * a.v_sm;
+        dma16(src, Vt + (i * NW + w) * 1024);
       }
     };
 
@@ -737,6 +757,36 @@ __device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int s
 // Work distribution shared by the kernel shapes: a persistent loop over the device-built
 // schedule (varlen), or one work item per work group (dense, split). run_item(it) runs one
 // work item with the kernel's LDS buffers.
+// The fused cache update's copy: the grid's threads share the chunk's K and V rows (16-byte
+// units), each written to the ring slot of its token (sink prefix, then the window).
+template <class K>
+__device__ __forceinline__ void kv_fused_update(const FwdArgs& a) {
+  typedef typename K::elem_t T;
+  constexpr int KU = K::kDQK / 8, VU = K::kDV / 8;   // 16-byte units per row
+  const int64_t rows = (int64_t)a.B * a.Hkv * a.upd_chunk;
+  const int64_t nk = rows * KU, n = nk + rows * VU;
+  const int64_t nthr = (int64_t)gridDim.x * gridDim.y * blockDim.x;
+  for (int64_t u = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; u < n;
+       u += nthr) {
+    const bool isv = u >= nk;
+    int64_t x = isv ? u - nk : u;
+    const int per = isv ? VU : KU;
+    const int piece = (int)(x % per);
+    x /= per;
+    const int row = (int)(x % a.upd_chunk);
+    x /= a.upd_chunk;
+    const int h = (int)(x % a.Hkv);
+    const int b = (int)(x / a.Hkv);
+    const int64_t tok = a.upd_tok0 + row;
+    const int64_t slot = tok < a.rm_sink ? tok : a.rm_sink + (tok - a.rm_sink) % a.rm_window;
+    const T* src = isv ? (const T*)a.vnew + b * a.vn_sb + h * a.vn_sh + row * a.vn_sm
+                       : (const T*)a.knew + b * a.kn_sb + h * a.kn_sh + row * a.kn_sm;
+    T* dst = isv ? (T*)a.v + b * a.v_sb + h * a.v_sh + slot * a.v_sm
+                 : (T*)a.k + b * a.k_sb + h * a.k_sh + slot * a.k_sm;
+    *reinterpret_cast<u32x4*>(dst + 8 * piece) = *reinterpret_cast<const u32x4*>(src + 8 * piece);
+  }
+}
+
 template <class K, int MODE, bool CAUSAL, class RunItem>
 __device__ __forceinline__ void attn_dispatch(const FwdArgs& a, const RunItem& run_item) {
   if constexpr (MODE == MODE_VARLEN) {
@@ -776,6 +826,7 @@ __device__ __forceinline__ void attn_dispatch(const FwdArgs& a, const RunItem& r
       __syncthreads();
     }
   } else if constexpr (MODE == MODE_SPLIT || MODE == MODE_SPLITP) {
+    if (MODE == MODE_SPLIT && a.kv_new) kv_fused_update<K>(a);
     const WorkItem it = decode_grid<K, CAUSAL>(a, blockIdx.x, blockIdx.y);
     run_item(it);
   } else {

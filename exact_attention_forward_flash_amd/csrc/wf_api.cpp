@@ -878,9 +878,13 @@ int wf_block_kv_init(wf_block_kv_state* s, int64_t cache_len, int64_t sink, int6
   return ok();
 }
 
-int wf_block_kv_cache_update(wf_block_kv_state* s, int64_t chunk_idx, const wf_tensor* k_new,
-                             const wf_tensor* v_new, wf_tensor* k_cache, wf_tensor* v_cache,
-                             void* stream) {
+}  // extern "C"
+
+// Checks of wf_block_kv_cache_update (also taken by the fused update + attend); *u16 is
+// cleared when rows or strides are not 16-byte multiples.
+static int check_update(const wf_block_kv_state* s, int64_t chunk_idx, const wf_tensor* k_new,
+                        const wf_tensor* v_new, const wf_tensor* k_cache, const wf_tensor* v_cache,
+                        bool* u16_out) {
   int rc;
   if ((rc = check_cache_state(s))) return rc;
   if (chunk_idx != s->last_chunk && chunk_idx != s->last_chunk + 1)
@@ -904,6 +908,20 @@ int wf_block_kv_cache_update(wf_block_kv_state* s, int64_t chunk_idx, const wf_t
       k_new->shape[3] != Dk || v_new->shape[0] != B || v_new->shape[1] != H ||
       v_new->shape[2] != s->chunk || v_new->shape[3] != Dv)
     return fail(WF_ERR_SHAPE, "updates must be [B,H,chunk,D] with chunk = %lld", (long long)s->chunk);
+  *u16_out = u16;
+  return WF_OK;
+}
+
+extern "C" {
+
+int wf_block_kv_cache_update(wf_block_kv_state* s, int64_t chunk_idx, const wf_tensor* k_new,
+                             const wf_tensor* v_new, wf_tensor* k_cache, wf_tensor* v_cache,
+                             void* stream) {
+  int rc;
+  bool u16 = true;
+  if ((rc = check_update(s, chunk_idx, k_new, v_new, k_cache, v_cache, &u16))) return rc;
+  const int64_t B = k_cache->shape[0], H = k_cache->shape[1], Dk = k_cache->shape[3];
+  const int64_t Dv = v_cache->shape[3];
   if (B * H > 0 && (Dk > 0 || Dv > 0)) {
     const int64_t kn[3] = {k_new->stride[0], k_new->stride[1], k_new->stride[2]};
     const int64_t vn[3] = {v_new->stride[0], v_new->stride[1], v_new->stride[2]};
@@ -966,9 +984,22 @@ size_t wf_block_kv_attend_workspace_size(const wf_block_kv_state* s, int B, int 
   return (size_t)(kMaxSplits * rows * ((int64_t)Dv + 1) * 4 + 256);
 }
 
-int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_tensor* k_cache,
+}  // extern "C"
+
+// The chunk a fused update + attend writes: its rows and first token.
+struct FusedUpdate {
+  const wf_tensor* k_new;
+  const wf_tensor* v_new;
+  int64_t tok0;
+};
+
+// wf_block_kv_attend over state s; with fu, the same launch also writes the chunk fu names
+// into the caches (s is then the state after that update) and reads its rows from fu's
+// tensors. dry: validate only, enqueue nothing.
+static int attend_impl(const wf_block_kv_state* s, const wf_tensor* q, const wf_tensor* k_cache,
                        const wf_tensor* v_cache, int is_causal, float scale, wf_tensor* out,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       const FusedUpdate* fu, bool dry) {
   int rc;
   if ((rc = check_cache_state(s))) return rc;
   if ((rc = check_data(q, "q", 4)) || (rc = check_data(k_cache, "k_cache", 4)) ||
@@ -994,8 +1025,9 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
     return fail(WF_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(WF_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (B * Hq * Lq == 0) return ok();
   if (s->cache_len > 0x7fffffff) return fail(WF_ERR_SHAPE, "cache_len exceeds 2^31");
+  if (dry) return WF_OK;
+  if (B * Hq * Lq == 0) return ok();
   int64_t T, head, start, n_vis;
   visible_range(s, &T, &head, &start, &n_vis);
   // The split kernel reads the visible tokens in chronological order through the slot map
@@ -1031,7 +1063,7 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   }
   // One split suffices when the query tiles alone fill the GPU: a non-causal attend does
   // not depend on the order of the keys, so the dense kernels read slots [0, n_vis) in place.
-  if (n_splits <= 1 && !causal && n_vis > 0)
+  if (n_splits <= 1 && !causal && n_vis > 0 && fu == nullptr)
     return run_dense(q, k_cache, v_cache, nullptr, wf::MASK_NONE, false, false, 0, sc, out, nullptr,
                      n_vis, (hipStream_t)stream);
   if (n_splits < 1) n_splits = 1;
@@ -1060,6 +1092,17 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   a.rm_sink = (int)s->sink;
   a.rm_off = (int)((start - s->sink) % s->window);
   a.rm_window = (int)s->window;
+  if (fu != nullptr) {
+    // the chunk is the newest `chunk` visible tokens
+    a.kv_new = 1;
+    a.new_lo = (int)(n_vis - s->chunk);
+    a.upd_chunk = (int)s->chunk;
+    a.upd_tok0 = fu->tok0;
+    a.knew = fu->k_new->data;
+    a.vnew = fu->v_new->data;
+    a.kn_sb = fu->k_new->stride[0]; a.kn_sh = fu->k_new->stride[1]; a.kn_sm = fu->k_new->stride[2];
+    a.vn_sb = fu->v_new->stride[0]; a.vn_sh = fu->v_new->stride[1]; a.vn_sm = fu->v_new->stride[2];
+  }
   const int64_t rows = B * Hq * Lq;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + (size_t)kMaxSplits * rows * Dv * 4);
@@ -1071,6 +1114,43 @@ int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_
                                              (int)Lq, (int)Dv, out->data, st(out, 0), st(out, 1),
                                              out->stride[2], nullptr, strm),
                     "combine launch");
+}
+
+extern "C" {
+
+int wf_block_kv_attend(const wf_block_kv_state* s, const wf_tensor* q, const wf_tensor* k_cache,
+                       const wf_tensor* v_cache, int is_causal, float scale, wf_tensor* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return attend_impl(s, q, k_cache, v_cache, is_causal, scale, out, workspace, workspace_bytes,
+                     stream, nullptr, false);
+}
+
+int wf_block_kv_update_attend(wf_block_kv_state* s, int64_t chunk_idx, const wf_tensor* k_new,
+                              const wf_tensor* v_new, wf_tensor* k_cache, wf_tensor* v_cache,
+                              const wf_tensor* q, int is_causal, float scale, wf_tensor* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  bool u16 = true;
+  if ((rc = check_update(s, chunk_idx, k_new, v_new, k_cache, v_cache, &u16))) return rc;
+  wf_block_kv_state after = *s;
+  after.last_chunk = chunk_idx;
+  if ((rc = attend_impl(&after, q, k_cache, v_cache, is_causal, scale, out, workspace,
+                        workspace_bytes, stream, nullptr, true)))
+    return rc;
+  const bool empty = q->shape[0] * q->shape[1] * q->shape[2] == 0 || numel(k_new) == 0;
+  if (!u16 || empty) {
+    // rows that are not 16-byte multiples (or nothing to attend): the two calls one by one
+    if ((rc = wf_block_kv_cache_update(s, chunk_idx, k_new, v_new, k_cache, v_cache, stream)))
+      return rc;
+    return wf_block_kv_attend(s, q, k_cache, v_cache, is_causal, scale, out, workspace,
+                              workspace_bytes, stream);
+  }
+  const FusedUpdate fu{k_new, v_new, chunk_idx * s->chunk};
+  if ((rc = attend_impl(&after, q, k_cache, v_cache, is_causal, scale, out, workspace,
+                        workspace_bytes, stream, &fu, false)))
+    return rc;
+  s->last_chunk = chunk_idx;
+  return ok();
 }
 
 size_t wf_sdpa_decode_workspace_size(const wf_tensor* q, const wf_tensor* k,

@@ -266,6 +266,19 @@ int wf_block_kv_attend(const wf_block_kv_state* st, const wf_tensor* q,
                        float scale, wf_tensor* out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* wf_block_kv_cache_update(st, chunk_idx, k_new, v_new, k_cache, v_cache) followed by
+ * wf_block_kv_attend(st, q, ...) in one attention launch (plus the combine): the attend's
+ * work groups also copy the chunk into its ring slots, and read the chunk's own rows from
+ * k_new / v_new (the slots they overwrite are not visible any more, so the launch never reads
+ * a slot it writes). Same arguments, checks, results and cache contents as the two calls;
+ * the workspace is the attend's. All checks of both calls run before anything is enqueued;
+ * on any error neither the state nor the caches change. Rows or strides that are not
+ * multiples of 16 bytes take the two calls one by one. */
+int wf_block_kv_update_attend(wf_block_kv_state* st, int64_t chunk_idx, const wf_tensor* k_new,
+                              const wf_tensor* v_new, wf_tensor* k_cache, wf_tensor* v_cache,
+                              const wf_tensor* q, int is_causal, float scale, wf_tensor* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable status name, and the thread-local detail of the last failed call. */
 const char* wf_status_string(int status);
 const char* wf_last_error(void);

@@ -297,3 +297,28 @@ def test_source_hash_follows_every_source_and_header(tmp_path, monkeypatch):
         assert b.source_hash() != base, rel
         p.write_bytes(text)
         assert b.source_hash() == base
+
+
+def test_fused_update_attend_checks_both_calls_before_anything(lib):
+    """The fused update + attend runs every check of the update and of the attend first: a
+    bad chunk index, bad update shapes or bad attend arguments leave the state unchanged.
+    Empty tensors (B = 0) pass the checks without a launch and commit the chunk."""
+    s, _ = _state(lib, 8, 2, 6, 2)
+
+    def call(idx, q=None, out=None, z=None, ws=FAKE, wsb=1 << 20):
+        z = z or T([0, 1, 2, 64], _lib.WF_F16)
+        c = T([0, 1, 8, 64], _lib.WF_F16)
+        q = q or T([0, 1, 2, 64], _lib.WF_F16)
+        out = out or T([0, 1, 2, 64], _lib.WF_F16)
+        return lib.wf_block_kv_update_attend(ctypes.byref(s), idx, ctypes.byref(z), ctypes.byref(z),
+                                             ctypes.byref(c), ctypes.byref(c), ctypes.byref(q), 0,
+                                             0.125, ctypes.byref(out), ws, wsb, None)
+    assert call(1) == ORDER and s.last_chunk == -1
+    assert call(0, z=T([0, 1, 3, 64], _lib.WF_F16)) == SHAPE and s.last_chunk == -1
+    assert call(0, q=T([0, 1, 2, 32], _lib.WF_F16)) == SHAPE and s.last_chunk == -1   # q width
+    assert call(0, out=T([0, 1, 3, 64], _lib.WF_F16)) == SHAPE and s.last_chunk == -1
+    assert call(0, ws=None) == WS and s.last_chunk == -1
+    assert call(0, q=T([0, 1, 2, 64], _lib.WF_F32)) == DTYPE and s.last_chunk == -1
+    assert call(0) == OK and s.last_chunk == 0
+    assert call(0) == OK and s.last_chunk == 0      # repeat
+    assert call(2) == ORDER and s.last_chunk == 0

@@ -210,3 +210,39 @@ def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H,
             ref, _ = oracle.sdpa(q1, kv, vv, is_causal=True, scale=sc, causal_align="bottom_right")
             assert_close(c.attend(q1.to(DEV), is_causal=True), ref, dt, f"one query, chunk {idx}")
         c.after_update(idx)
+
+
+@pytest.mark.parametrize("sink,window,chunk,H,Hkv,causal", [
+    (64, 448, 64, 2, 2, False), (0, 256, 64, 4, 1, True), (256, 3840, 256, 24, 24, False),
+    (32, 96, 32, 8, 2, True)])
+def test_fused_update_attend_matches_the_two_calls(sink, window, chunk, H, Hkv, causal):
+    """update_attend gives the output of update then attend (bit for bit when the attend takes
+    the split kernel too; a non-causal attend over a single key split may take a dense kernel
+    instead, which rounds differently) and leaves the same cache contents, across the roll of
+    the window and a repeated chunk."""
+    D = 128
+    shape = (1, Hkv, sink + window, D)
+    a = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=torch.float16)
+    b = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=torch.float16)
+    g = torch.Generator().manual_seed(sink + window + H)
+    steps = min((sink + window) // chunk + 4, 20)
+    order = list(range(steps))
+    order.insert(5, 4)                      # chunk 4 again: overwrite
+    for idx in order:
+        k = torch.randn(1, Hkv, chunk, D, generator=g).half().to(DEV)
+        v = torch.randn(1, Hkv, chunk, D, generator=g).half().to(DEV)
+        q = torch.randn(1, H, chunk, D, generator=g).half().to(DEV)
+        a.before_update(idx)
+        a.update(k, v)
+        ref = a.attend(q, is_causal=causal)
+        a.after_update(idx)
+        b.before_update(idx)
+        got = b.update_attend(k, v, q, is_causal=causal)
+        b.after_update(idx)
+        if causal:
+            assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"chunk {idx}"
+        else:
+            d = (got.float() - ref.float()).abs()
+            assert d.max().item() < 4e-3 and d.mean().item() < 2e-4, f"chunk {idx}: {d.max().item()}"
+        assert torch.equal(a.k, b.k) and torch.equal(a.v, b.v), f"cache after chunk {idx}"
+        assert a.last_chunk == b.last_chunk == idx

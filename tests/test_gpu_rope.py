@@ -33,6 +33,8 @@ CASES = [  # dtype, B, Hq, Hkv, Lq, Lk, D, rot, style, q_pos0, k_pos0, causal
     # (the persistent kernel turns Q as it reads it)
     ("bf16", 2, 8, 2, 200, 200, 128, 64, 1, 0, 0, True),
     ("fp16", 1, 16, 4, 257, 257, 128, 64, 1, 7, 7, True),
+    ("bf16", 1, 8, 2, 190, 190, 64, 32, 1, 3, 3, True),
+    ("fp16", 2, 4, 1, 129, 129, 64, 64, 1, 0, 0, True),
 ]
 
 
@@ -56,8 +58,9 @@ def test_rope_shapes(case):
     assert np.abs(to64(lse)[live] - ref_lse[live]).max() < tol
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[6], CASES[7]],
-                         ids=["rotate-half", "interleaved", "interleaved-gqa4-bf16", "interleaved-gqa4-fp16"])
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[6], CASES[7], CASES[8], CASES[9]],
+                         ids=["rotate-half", "interleaved", "interleaved-gqa4-bf16", "interleaved-gqa4-fp16",
+                              "interleaved-gqa4-bf16-d64", "interleaved-gqa4-fp16-d64"])
 def test_rope_separate_pass_path(case):
     """These cases (rotate-half over the whole head, causal GQA; interleaved over half the
     head, also causal with four query heads per KV head) turn Q in the persistent kernel's
@@ -67,7 +70,8 @@ def test_rope_separate_pass_path(case):
         test_rope_shapes(case)
 
 
-@pytest.mark.parametrize("case", [CASES[6], CASES[7]], ids=["bf16", "fp16"])
+@pytest.mark.parametrize("case", [CASES[6], CASES[7], CASES[8], CASES[9]],
+                         ids=["bf16", "fp16", "bf16-d64", "fp16-d64"])
 def test_rope_interleaved_gqa_without_lse(case):
     """Without the lse the persistent kernel takes its prescaled-Q variant, which turns Q and
     then multiplies it by scale*log2(e); its output matches the oracle and the separate-pass
