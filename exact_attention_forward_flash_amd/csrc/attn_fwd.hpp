@@ -43,7 +43,8 @@ enum { MASK_NONE = 0, MASK_BOOL = 1, MASK_HALF = 2, MASK_F32 = 3 };
 // MODE_DENSE_Q: the persistent 64-query-wave kernel (attn_fwd_q.hpp), calls without the lse.
 enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3, MODE_DENSE_P16 = 4,
        MODE_SPLITP = 5, MODE_DENSE_PR = 6, MODE_DENSE_PR16 = 7, MODE_DENSE_PI = 8,
-       MODE_DENSE_PI16 = 9, MODE_DENSE_Q = 10 };
+       MODE_DENSE_PI16 = 9, MODE_DENSE_Q = 10,
+       MODE_SPLITU = 11 };   // split-KV over the block KV cache with the fused chunk update
 
 struct FwdArgs {
   const void* q; const void* q2; const void* k; const void* k2; const void* v;
@@ -75,10 +76,10 @@ struct FwdArgs {
   // block KV cache (split mode): key row t is the t-th visible token in chronological order,
   // held in slot t (t < rm_head: the sink) or rm_sink + (rm_off + t - rm_head) mod rm_window
   int kv_remap, rm_head, rm_sink, rm_off, rm_window;
-  // fused cache update (split mode): the chunk's new K / V rows [B, Hkv, upd_chunk, d] are
+  // fused cache update (MODE_SPLITU): the chunk's new K / V rows [B, Hkv, upd_chunk, d] are
   // read for key rows >= new_lo straight from knew / vnew, and the work groups also copy
   // them into their ring slots (tokens upd_tok0 ..) of the caches a.k / a.v
-  int kv_new, new_lo, upd_chunk;
+  int new_lo, upd_chunk, upd_off;
   const void* knew; const void* vnew;
   int64_t kn_sb, kn_sh, kn_sm, vn_sb, vn_sh, vn_sm;
   int64_t upd_tok0;
@@ -215,51 +216,71 @@ struct AttnFwd {
     // swizzled position p%KCH, which holds logical chunk (p%KCH) ^ swizzle(row).
     const T* ksrc[KLOADS];
     int64_t kstride[KLOADS];
-    int krow[KLOADS];
+    int krow[KLOADS], kcol[KLOADS];
 #pragma unroll
     for (int i = 0; i < KLOADS; ++i) {
       const int p = (i * NW + w) * 64 + lane;
       const int r = p / KCH, pos = p % KCH;
       const int col = (pos ^ kswz(r)) * 8;
       krow[i] = r;
+      kcol[i] = col;
       if (DQK1 == DQK || col < DQK1) { ksrc[i] = kp + col; kstride[i] = a.k_sm; }
       else { ksrc[i] = k2p + (col - DQK1); kstride[i] = a.k2_sm; }
     }
     const T* vsrc[VLOADS];
-    int vrow[VLOADS];
+    int vrow[VLOADS], vcol[VLOADS];
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int p = (i * NW + w) * 64 + lane;
       const int pc = p < BN * VCH ? p : BN * VCH - 1;   // past the tile: never issued
       const int r = pc / VCH, pos = pc % VCH;
       vrow[i] = r;
-      vsrc[i] = vp + ((pos ^ vswz(r)) * 8);
+      vcol[i] = (pos ^ vswz(r)) * 8;
+      vsrc[i] = vp + vcol[i];
     }
     const int lk_last = it.Lk - 1;
     // Memory row of key row r: r itself, or (block KV cache) the slot of the r-th visible
     // token, so that key rows run in chronological order whatever the ring's rotation.
+    constexpr bool kSplitMode = MODE == MODE_SPLIT || MODE == MODE_SPLITU;
+    const int rm_on = kSplitMode ? a.kv_remap : 0, rm_head = kSplitMode ? a.rm_head : 0;
+    const int rm_off = kSplitMode ? a.rm_off : 0, rm_window = kSplitMode ? a.rm_window : 1;
+    const int rm_sink = kSplitMode ? a.rm_sink : 0;
     auto key_row = [&](int r) {
-      if (MODE != MODE_SPLIT || !a.kv_remap || r < a.rm_head) return r;
-      int x = a.rm_off + (r - a.rm_head);   // < 2 * rm_window
-      x = x >= a.rm_window ? x - a.rm_window : x;
-      return a.rm_sink + x;
+      if constexpr (!kSplitMode) return r;
+      int x = rm_off + (r - rm_head);   // < 2 * rm_window when r >= rm_head
+      x = x >= rm_window ? x - rm_window : x;
+      return (rm_on && r >= rm_head) ? rm_sink + x : r;   // selects, no branch
     };
     // Rows past the last key are clamped onto it: their scores are masked to -inf, and
     // the duplicated V rows meet p = 0.
     // Fused cache update: rows of the new chunk come from its own tensors (same bits as the
     // slots the update writes, which this launch does not read).
-    const bool fresh = MODE == MODE_SPLIT && a.kv_new;
-    const T* knb = fresh ? (const T*)a.knew + it.b * a.kn_sb + g * a.kn_sh : nullptr;
-    const T* vnb = fresh ? (const T*)a.vnew + it.b * a.vn_sb + g * a.vn_sh : nullptr;
+    constexpr bool fresh = MODE == MODE_SPLITU;
+    // uniform values of the fresh-row addressing, read once: a new row's element offset from
+    // the cache head base is (new head base - cache head base) + (r - new_lo) * row stride
+    const int new_lo = fresh ? a.new_lo : 0;
+    const int64_t kn_sm = fresh ? a.kn_sm : 0, vn_sm = fresh ? a.vn_sm : 0;
+    const int64_t kn_delta =
+        fresh ? (int64_t)(((const T*)a.knew + it.b * a.kn_sb + g * a.kn_sh) - kp) : 0;
+    const int64_t vn_delta =
+        fresh ? (int64_t)(((const T*)a.vnew + it.b * a.vn_sb + g * a.vn_sh) - vp) : 0;
+    const int64_t k_sm = a.k_sm, v_sm = a.v_sm;
+    // With the fused update a lane's row comes from one of two uniform bases (cache or new
+    // chunk) at its column: only the column offset is kept per copy.
     auto issue_k = [&](int kt, WF_LDS char* Kt) {
       const int k0 = kt * BN;
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i) {
         int r = k0 + krow[i];
         r = r < lk_last ? r : lk_last;
-        const T* src = (fresh && r >= a.new_lo)
-                           ? knb + (ksrc[i] - kp) + (int64_t)(r - a.new_lo) * a.kn_sm
-                           : ksrc[i] + (int64_t)key_row(r) * kstride[i];
+        const T* src;
+        if constexpr (fresh) {
+          const int64_t off = r >= new_lo ? kn_delta + (int64_t)(r - new_lo) * kn_sm
+                                          : (int64_t)key_row(r) * k_sm;
+          src = kp + kcol[i] + off;
+        } else {
+          src = ksrc[i] + (int64_t)key_row(r) * kstride[i];
+        }
         dma16(src, Kt + (i * NW + w) * 1024);
       }
     };
@@ -270,9 +291,14 @@ struct AttnFwd {
         if ((BN * VCH) % NT != 0 && (i * NW + w) * 64 >= BN * VCH) continue;  // wave-uniform
         int r = k0 + vrow[i];
         r = r < lk_last ? r : lk_last;
-        const T* src = (fresh && r >= a.new_lo)
-                           ? vnb + (vsrc[i] - vp) + (int64_t)(r - a.new_lo) * a.vn_sm
-                           : vsrc[i] + (int64_t)key_row(r) * a.v_sm;
+        const T* src;
+        if constexpr (fresh) {
+          const int64_t off = r >= new_lo ? vn_delta + (int64_t)(r - new_lo) * vn_sm
+                                          : (int64_t)key_row(r) * v_sm;
+          src = vp + vcol[i] + off;
+        } else {
+          src = vsrc[i] + (int64_t)key_row(r) * v_sm;
+        }
         dma16(src, Vt + (i * NW + w) * 1024);
       }
     };
@@ -671,7 +697,7 @@ struct AttnFwd {
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const float lse2 = l > 0.f ? (m_run == -INFINITY ? 0.f : m_run) + __builtin_log2f(l) : -INFINITY;
     if (row_ok) {
-      if constexpr (MODE == MODE_SPLIT || MODE == MODE_SPLITP) {
+      if constexpr (MODE == MODE_SPLIT || MODE == MODE_SPLITP || MODE == MODE_SPLITU) {
         const int64_t row = (((int64_t)it.split * a.B + it.b) * a.Hq + hq_l) * a.Lq + qpos;
         float* dst = a.part_o + row * DV;
 #pragma unroll
@@ -758,27 +784,32 @@ __device__ __forceinline__ WorkItem decode_grid(const FwdArgs& a, int bid, int s
 // schedule (varlen), or one work item per work group (dense, split). run_item(it) runs one
 // work item with the kernel's LDS buffers.
 // The fused cache update's copy: the grid's threads share the chunk's K and V rows (16-byte
-// units), each written to the ring slot of its token (sink prefix, then the window).
+// units), each written to the ring slot of its token (sink prefix, then the window). Index
+// arithmetic in 32 bits (the host bounds rows * units below 2^31); a row's slot is
+// rm_sink + (upd_off + row) folded once into the window, or the token itself in the sink.
 template <class K>
 __device__ __forceinline__ void kv_fused_update(const FwdArgs& a) {
   typedef typename K::elem_t T;
   constexpr int KU = K::kDQK / 8, VU = K::kDV / 8;   // 16-byte units per row
-  const int64_t rows = (int64_t)a.B * a.Hkv * a.upd_chunk;
-  const int64_t nk = rows * KU, n = nk + rows * VU;
-  const int64_t nthr = (int64_t)gridDim.x * gridDim.y * blockDim.x;
-  for (int64_t u = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; u < n;
-       u += nthr) {
+  const int rows = a.B * a.Hkv * a.upd_chunk;
+  const int nk = rows * KU, n = nk + rows * VU;
+  const int nthr = gridDim.x * gridDim.y * blockDim.x;
+  for (int u = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x; u < n; u += nthr) {
     const bool isv = u >= nk;
-    int64_t x = isv ? u - nk : u;
-    const int per = isv ? VU : KU;
-    const int piece = (int)(x % per);
-    x /= per;
-    const int row = (int)(x % a.upd_chunk);
-    x /= a.upd_chunk;
-    const int h = (int)(x % a.Hkv);
-    const int b = (int)(x / a.Hkv);
-    const int64_t tok = a.upd_tok0 + row;
-    const int64_t slot = tok < a.rm_sink ? tok : a.rm_sink + (tok - a.rm_sink) % a.rm_window;
+    const int x = isv ? u - nk : u;
+    const int piece = isv ? x % VU : x % KU;
+    const int rr = isv ? x / VU : x / KU;       // (b, h, row) flattened
+    const int row = rr % a.upd_chunk;
+    const int bh = rr / a.upd_chunk;
+    const int h = bh % a.Hkv, b = bh / a.Hkv;
+    int64_t slot;
+    if (a.upd_tok0 + row < a.rm_sink) {
+      slot = a.upd_tok0 + row;
+    } else {
+      int xo = a.upd_off + row;
+      xo = xo >= a.rm_window ? xo - a.rm_window : xo;
+      slot = a.rm_sink + xo;
+    }
     const T* src = isv ? (const T*)a.vnew + b * a.vn_sb + h * a.vn_sh + row * a.vn_sm
                        : (const T*)a.knew + b * a.kn_sb + h * a.kn_sh + row * a.kn_sm;
     T* dst = isv ? (T*)a.v + b * a.v_sb + h * a.v_sh + slot * a.v_sm
@@ -825,8 +856,8 @@ __device__ __forceinline__ void attn_dispatch(const FwdArgs& a, const RunItem& r
       run_item(it);
       __syncthreads();
     }
-  } else if constexpr (MODE == MODE_SPLIT || MODE == MODE_SPLITP) {
-    if (MODE == MODE_SPLIT && a.kv_new) kv_fused_update<K>(a);
+  } else if constexpr (MODE == MODE_SPLIT || MODE == MODE_SPLITP || MODE == MODE_SPLITU) {
+    if constexpr (MODE == MODE_SPLITU) kv_fused_update<K>(a);
     const WorkItem it = decode_grid<K, CAUSAL>(a, blockIdx.x, blockIdx.y);
     run_item(it);
   } else {

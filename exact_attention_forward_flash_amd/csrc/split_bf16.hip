@@ -25,6 +25,17 @@ const AttnEntry* attn_table_split_bf16(int* n) {
   *n = (int)(sizeof(kTable) / sizeof(kTable[0]));
   return kTable;
 }
+// block KV cache attend with the chunk update fused into the launch
+#define U(D, HPW, CAUSAL) WF_ATTN_ENTRY(__bf16, DT_BF16, D, D, D, 4, HPW, MASK_NONE, CAUSAL, MODE_SPLITU)
+static const AttnEntry kTableU[] = {
+    U(64, 1, false),  U(64, 2, false),  U(64, 4, false),  U(64, 1, true),  U(64, 2, true),  U(64, 4, true),
+    U(128, 1, false), U(128, 2, false), U(128, 4, false), U(128, 1, true), U(128, 2, true), U(128, 4, true),
+};
+#undef U
+const AttnEntry* attn_table_splitu_bf16(int* n) {
+  *n = (int)(sizeof(kTableU) / sizeof(kTableU[0]));
+  return kTableU;
+}
 const AttnEntry* attn_table_splitp_bf16(int* n) {
   *n = (int)(sizeof(kTableP) / sizeof(kTableP[0]));
   return kTableP;

@@ -152,7 +152,8 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
                                    wf::attn_table_mla,           wf::attn_table_mla_v64,
                                    wf::attn_table_split_bf16,
                                    wf::attn_table_split_f16,     wf::attn_table_splitp_bf16,
-                                   wf::attn_table_splitp_f16,
+                                   wf::attn_table_splitp_f16,    wf::attn_table_splitu_bf16,
+                                   wf::attn_table_splitu_f16,
                                    wf::attn_table_w_bf16_d64,    wf::attn_table_w_bf16_d128,
                                    wf::attn_table_w_f16_d64,     wf::attn_table_w_f16_d128,
                                    wf::attn_table_p_bf16_d64,    wf::attn_table_p_bf16_d128,
@@ -1037,9 +1038,9 @@ static int attend_impl(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   const int64_t G = Hq / Hkv;
   const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
   const int causal = is_causal ? 1 : 0;
-  const int nw = (hpw == 1 && !causal && tune(T_ATTEND_NW) == 8) ? 8 : 4;
+  const int nw = (hpw == 1 && !causal && fu == nullptr && tune(T_ATTEND_NW) == 8) ? 8 : 4;
   const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, nw, hpw, wf::MASK_NONE, causal,
-                                     wf::MODE_SPLIT);
+                                     fu != nullptr ? wf::MODE_SPLITU : wf::MODE_SPLIT);
   if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
   const int n_kt = (int)((n_vis + e->bn - 1) / e->bn);
   const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
@@ -1094,10 +1095,12 @@ static int attend_impl(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   a.rm_window = (int)s->window;
   if (fu != nullptr) {
     // the chunk is the newest `chunk` visible tokens
-    a.kv_new = 1;
     a.new_lo = (int)(n_vis - s->chunk);
     a.upd_chunk = (int)s->chunk;
     a.upd_tok0 = fu->tok0;
+    // window offset of the chunk's first token past the sink (negative while the chunk
+    // still overlaps the sink: its rows past the sink then need no folding)
+    a.upd_off = (int)(fu->tok0 >= s->sink ? (fu->tok0 - s->sink) % s->window : fu->tok0 - s->sink);
     a.knew = fu->k_new->data;
     a.vnew = fu->v_new->data;
     a.kn_sb = fu->k_new->stride[0]; a.kn_sh = fu->k_new->stride[1]; a.kn_sm = fu->k_new->stride[2];
@@ -1140,6 +1143,13 @@ int wf_block_kv_update_attend(wf_block_kv_state* s, int64_t chunk_idx, const wf_
   const bool empty = q->shape[0] * q->shape[1] * q->shape[2] == 0 || numel(k_new) == 0;
   if (!u16 || empty) {
     // rows that are not 16-byte multiples (or nothing to attend): the two calls one by one
+    if ((rc = wf_block_kv_cache_update(s, chunk_idx, k_new, v_new, k_cache, v_cache, stream)))
+      return rc;
+    return wf_block_kv_attend(s, q, k_cache, v_cache, is_causal, scale, out, workspace,
+                              workspace_bytes, stream);
+  }
+  const int64_t units = q->shape[0] * k_cache->shape[1] * s->chunk * (k_cache->shape[3] + v_cache->shape[3]) / 8;
+  if (units >= ((int64_t)1 << 31)) {   // beyond the fused copy's 32-bit indexing: two calls
     if ((rc = wf_block_kv_cache_update(s, chunk_idx, k_new, v_new, k_cache, v_cache, stream)))
       return rc;
     return wf_block_kv_attend(s, q, k_cache, v_cache, is_causal, scale, out, workspace,

@@ -38,6 +38,8 @@ const AttnEntry* attn_table_split_bf16(int* n);
 const AttnEntry* attn_table_split_f16(int* n);
 const AttnEntry* attn_table_splitp_bf16(int* n);
 const AttnEntry* attn_table_splitp_f16(int* n);
+const AttnEntry* attn_table_splitu_bf16(int* n);
+const AttnEntry* attn_table_splitu_f16(int* n);
 const AttnEntry* attn_table_w_bf16_d128(int* n);
 const AttnEntry* attn_table_w_bf16_d64(int* n);
 const AttnEntry* attn_table_w_f16_d128(int* n);
