@@ -44,7 +44,8 @@ enum { MASK_NONE = 0, MASK_BOOL = 1, MASK_HALF = 2, MASK_F32 = 3 };
 enum { MODE_DENSE = 0, MODE_VARLEN = 1, MODE_SPLIT = 2, MODE_DENSE_P = 3, MODE_DENSE_P16 = 4,
        MODE_SPLITP = 5, MODE_DENSE_PR = 6, MODE_DENSE_PR16 = 7, MODE_DENSE_PI = 8,
        MODE_DENSE_PI16 = 9, MODE_DENSE_Q = 10,
-       MODE_SPLITU = 11 };   // split-KV over the block KV cache with the fused chunk update
+       MODE_SPLITU = 11,     // split-KV over the block KV cache with the fused chunk update
+       MODE_DENSE_PM = 12 }; // dense with a mask, no lse: Q prescaled, scores from -m (see PRE)
 
 struct FwdArgs {
   const void* q; const void* q2; const void* k; const void* k2; const void* v;
@@ -132,7 +133,8 @@ struct AttnFwd {
   // keys) is copied into LDS with the K tile (coalesced), instead of every lane reading its own
   // row from global memory (32 rows per load instruction).
   static constexpr int MSZ = MASK == MASK_BOOL ? 1 : MASK == MASK_HALF ? 2 : 4;
-  static constexpr bool MLDS = (MASK == MASK_BOOL || MASK == MASK_HALF) && HPW == 1 && MODE == MODE_DENSE;
+  static constexpr bool MLDS = (MASK == MASK_BOOL || MASK == MASK_HALF) && HPW == 1 &&
+                               (MODE == MODE_DENSE || MODE == MODE_DENSE_PM);
   static constexpr int MROWB = BN * MSZ;                 // bytes of one row of a mask tile
   static constexpr int MCPR = MROWB / 16;                // its 16-byte chunks
   // chunk swizzle of mask tile rows in LDS (position = chunk ^ mswz(row))
@@ -178,6 +180,14 @@ struct AttnFwd {
     const float c = a.scale_log2;
 
     constexpr bool PACK = MODE == MODE_SPLITP;
+    // PRE (masked dense calls without the lse): Q is multiplied by scale*log2(e) and rounded
+    // back to the input type once, and the S^T accumulators start from -m_ref, so the MFMAs
+    // give log2-domain scores relative to the reference max and the weights are exp2 of them
+    // with no per-score FMA (the VALU work per score is what bounds masked calls at small head
+    // dims). The rounding of the scaled Q changes every score of a row by a common factor of
+    // order 1e-4, as in the persistent kernel without the lse; calls asking for the lse keep
+    // the exact form.
+    constexpr bool PRE = MODE == MODE_DENSE_PM;
     static_assert(!PACK || (HPW == 1 && MASK == MASK_NONE && DQK1 == DQK), "packed rows: plain split only");
     const T* qp = (const T*)a.q + it.b * a.q_sb + hq * a.q_sh + it.qtok0 * a.q_sm;
     const T* q2p = (const T*)a.q2 + it.b * a.q2_sb + hq * a.q2_sh + it.qtok0 * a.q2_sm;
@@ -209,6 +219,13 @@ struct AttnFwd {
         src = (16 * s < DQK1) ? qp + (int64_t)qrow_c * a.q_sm + col
                               : q2p + (int64_t)qrow_c * a.q2_sm + (col - DQK1);
       qf[s] = *reinterpret_cast<const u32x4*>(src);
+      if constexpr (PRE) {
+        typedef typename Mfma16<T>::v8 v8;
+        v8 x = __builtin_bit_cast(v8, qf[s]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (T)((float)x[e] * a.scale_log2);
+        qf[s] = __builtin_bit_cast(u32x4, x);
+      }
     }
 
     // ---- per-thread copy descriptors for the K and V tiles ---------------------------
@@ -373,6 +390,9 @@ struct AttnFwd {
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
+    // PRE: m_ref is the reference the pending tile's scores were computed against (m_run, or 0
+    // while m_run is -inf).
+    float m_ref = 0.f;
 
     // Tiles this wave computes: [kt_lo, kt_live). With causal masking a wave is done once a
     // tile starts past its last query; it still copies tiles and meets the barriers.
@@ -463,7 +483,7 @@ struct AttnFwd {
                 // convert, then an fp32 FMA: the fused mixed-precision FMA measured slower
                 float mv = (float)hv[kb][r >> 2][r & 3];
                 asm volatile("" : "+v"(mv));
-                sc[kb][r] = fmaf(mv, a.inv_scale, sc[kb][r]);
+                sc[kb][r] = fmaf(mv, PRE ? kLog2e : a.inv_scale, sc[kb][r]);
               }
           }
         } else {
@@ -509,7 +529,7 @@ struct AttnFwd {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               if constexpr (MASK == MASK_BOOL) sc[kb][r] += mval[kb][r >> 2][r & 3];
-              else sc[kb][r] = fmaf(mval[kb][r >> 2][r & 3], a.inv_scale, sc[kb][r]);
+              else sc[kb][r] = fmaf(mval[kb][r >> 2][r & 3], PRE ? kLog2e : a.inv_scale, sc[kb][r]);
             }
         }
       }
@@ -532,7 +552,7 @@ struct AttnFwd {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[kb][r] = PRE ? -m_ref : 0.f;
       u32x4 k0f = kfrag(Kt, 0, 0), k1f = kfrag(Kt, 0, 1);
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -550,19 +570,30 @@ struct AttnFwd {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      return xhalf_max(mx) * c;
+      return PRE ? xhalf_max(mx) : xhalf_max(mx) * c;
     };
     // Raise the reference max (rescaling O and l) only when a query's tile max passes it
     // by more than 8, so p = exp2(t - m) stays <= 2^8.
-    auto rescale = [&](float mt) {
+    // PRE: mt is relative to m_ref, and a moved reference shifts the pending tile onto it.
+    auto rescale = [&](float mt, f32x16* cur) {
+      if (PRE) mt += m_ref;
       if (wave_any(mt > m_run + 8.0f)) {
         const float m_new = fmaxf(m_run, mt);
-        const float alpha = fast_exp2(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        const float m_new_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_new_ref);
         l_run *= alpha;
 #pragma unroll
         for (int n = 0; n < NDV; ++n)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
+        if constexpr (PRE) {
+          const float d = m_new_ref - m_ref;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cur[kb][r] -= d;
+          m_ref = m_new_ref;
+        }
         m_run = m_new;
       }
     };
@@ -586,7 +617,7 @@ struct AttnFwd {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) nxt[kb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) nxt[kb][r] = PRE ? -m_ref : 0.f;
         u32x4 k0f = kfrag(Kn, 0, 0), k1f = kfrag(Kn, 0, 1);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -595,9 +626,9 @@ struct AttnFwd {
           nxt[0] = Mfma16<T>::run(k0f, qf[s], nxt[0]);
 #pragma unroll
           for (int e = s * 32 / NS; e < (s + 1) * 32 / NS; ++e) {
-            const float p = fast_exp2(fmaf(cur[e >> 4][e & 15], c, neg_m));
+            const float p = fast_exp2(PRE ? cur[e >> 4][e & 15] : fmaf(cur[e >> 4][e & 15], c, neg_m));
             cur[e >> 4][e & 15] = p;
-            psum += p;
+            if (!PRE) psum += p;
           }
           nxt[1] = Mfma16<T>::run(k1f, qf[s], nxt[1]);
           k0f = n0; k1f = n1;
@@ -605,12 +636,12 @@ struct AttnFwd {
       } else {
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
-          const float p = fast_exp2(fmaf(cur[e >> 4][e & 15], c, neg_m));
+          const float p = fast_exp2(PRE ? cur[e >> 4][e & 15] : fmaf(cur[e >> 4][e & 15], c, neg_m));
           cur[e >> 4][e & 15] = p;
-          psum += p;
+          if (!PRE) psum += p;
         }
       }
-      l_run += psum;
+      if (!PRE) l_run += psum;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         pk[m] = pack8<T>(cur[m >> 1], 8 * (m & 1));
@@ -627,6 +658,7 @@ struct AttnFwd {
 #pragma unroll
       for (int n = 0; n < NDV; ++n) vf[n] = vfrag(Vc, 0, n);
       float mx = -INFINITY;
+      float lp[2] = {0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         u32x4 vn[NDV];
@@ -634,6 +666,8 @@ struct AttnFwd {
         for (int n = 0; n < NDV; ++n) vn[n] = m + 1 < 4 ? vfrag(Vc, m + 1, n) : vf[n];
 #pragma unroll
         for (int n = 0; n < NDV; ++n) oacc[n] = Mfma16<T>::run(vf[n], pk[m], oacc[n]);
+        // PRE: row sums over the packed 16-bit weights (exactly the weights that multiply V)
+        if constexpr (PRE) lp[m & 1] = sum8_acc<T>(pk[m], lp[m & 1]);
         if constexpr (has_next) {
 #pragma unroll
           for (int e = 8 * m; e < 8 * m + 8; ++e) mx = fmaxf(mx, nxt[e >> 4][e & 15]);
@@ -641,7 +675,12 @@ struct AttnFwd {
 #pragma unroll
         for (int n = 0; n < NDV; ++n) vf[n] = vn[n];
       }
-      if constexpr (has_next) mt_cur = xhalf_max(mx) * c;
+      if constexpr (PRE) {
+        // 3 wait states between the last v_dot2c write and an ordinary VALU read of it
+        asm volatile("s_nop 2" : "+v"(lp[0]), "+v"(lp[1]));
+        l_run += lp[0] + lp[1];
+      }
+      if constexpr (has_next) mt_cur = PRE ? xhalf_max(mx) : xhalf_max(mx) * c;
     };
 
     // ---- key-tile loop -----------------------------------------------------------------------
@@ -676,7 +715,7 @@ struct AttnFwd {
           // The next tile's S^T and row max are always computed: on this wave's last live
           // tile they read a stale K buffer and the result is never used. This keeps both
           // phases branch-free for the scheduler.
-          rescale(mt_cur);
+          rescale(mt_cur, cur);
           phase_a(Kn, std::true_type(), cur, nxt);
           if (u + 1 < n_live && need_mask(it.kt_lo + u + 1)) apply_mask(it.kt_lo + u + 1, nxt);
           phase_b(Vc, std::true_type(), nxt);

@@ -9,6 +9,9 @@ static const AttnEntry kTable[] = {
     E(8, 1, MASK_BOOL, false), E(8, 1, MASK_HALF, false), E(8, 1, MASK_F32, false),
     E(4, 1, MASK_NONE, false), E(4, 2, MASK_NONE, false), E(4, 4, MASK_NONE, false),
     E(4, 1, MASK_NONE, true),  E(4, 2, MASK_NONE, true),  E(4, 4, MASK_NONE, true),
+    // masked calls without the lse: Q prescaled, scores relative to the reference max
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 64, 64, 64, 8, 1, MASK_BOOL, false, MODE_DENSE_PM),
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 64, 64, 64, 8, 1, MASK_HALF, false, MODE_DENSE_PM),
 };
 #undef E
 const AttnEntry* attn_table_sdpa_bf16_d64(int* n) {

@@ -112,10 +112,11 @@ int check_cache_data(const wf_tensor* t, const char* name, bool* unit16) {
 // once on first use, then changed only through wf_tune_set. -1 = automatic choice.
 enum TuneKey { T_HPW, T_PERSIST, T_Q64, T_QPW, T_NW, T_DECODE_PACK, T_DECODE_GROUPS,
                T_DECODE_MIN_TILES, T_MLA_XCD, T_ATTEND_GROUPS, T_ATTEND_NW, T_ATTEND_MIN_TILES,
-               T_COUNT };
+               T_MASK_PRE, T_COUNT };
 const char* const kTuneNames[T_COUNT] = {"hpw", "persist", "q64", "qpw", "nw", "decode_pack",
                                          "decode_groups", "decode_min_tiles", "mla_xcd",
-                                         "attend_groups", "attend_nw", "attend_min_tiles"};
+                                         "attend_groups", "attend_nw", "attend_min_tiles",
+                                         "mask_pre"};
 std::atomic<int>* tune_table() {
   static std::atomic<int> t[T_COUNT];
   static std::once_flag once;
@@ -359,7 +360,11 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   if (tune(T_QPW) == 32) qpw = 32;
   else if (tune(T_QPW) == 64 && w64_ok) qpw = 64;
   const wf::AttnEntry* e = nullptr;
-  if (qpw == 64) e = find_attn(dt, Dqk, Dqk, Dv, 4, hpw, mask_kind, causal, wf::MODE_DENSE, 64);
+  // Bool / 16-bit masked calls without the lse: the prescaled form (no per-score FMA); fp32
+  // masks keep the exact form (the prescaled one spills registers with them).
+  if (mask_kind != wf::MASK_NONE && lse == nullptr && !causal && tune(T_MASK_PRE) != 0)
+    e = find_attn(dt, Dqk, Dqk, Dv, 8, hpw, mask_kind, 0, wf::MODE_DENSE_PM, 32);
+  if (!e && qpw == 64) e = find_attn(dt, Dqk, Dqk, Dv, 4, hpw, mask_kind, causal, wf::MODE_DENSE, 64);
   if (!e) {
     int nw = 8;
     if (tune(T_NW) == 4 && mask_kind == wf::MASK_NONE) nw = 4;

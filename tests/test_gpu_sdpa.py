@@ -312,12 +312,16 @@ def test_causal_gqa_prefill_full_size_sampled(qpw):
 
 
 @pytest.mark.parametrize("kind", ["bool", "float"])
-def test_masked_sdpa_full_size(kind):
-    """B=2, H=16, L=2048, d=64 fp16 with a [2,1,L,L] mask broadcast over heads, fully checked."""
+@pytest.mark.parametrize("pre", [True, False], ids=["prescaled", "exact"])
+def test_masked_sdpa_full_size(kind, pre):
+    """B=2, H=16, L=2048, d=64 fp16 with a [2,1,L,L] mask broadcast over heads, fully checked,
+    through the prescaled-Q kernel (the default without the lse) and the exact one."""
     w = masked_sdpa_inputs(kind)
-    out = run(w)
+    with tune(mask_pre=-1 if pre else 0):
+        out = run(w)
     ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w["mask"], scale=np.float32(w["scale"]))
-    assert_close(out, ref, torch.float16, f"masked {kind}")
+    mx, mean = assert_close(out, ref, torch.float16, f"masked {kind}")
+    print(f"masked {kind} {'prescaled' if pre else 'exact'}: max {mx:.3g} mean {mean:.3g}")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp16"])

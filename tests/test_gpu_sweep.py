@@ -190,19 +190,30 @@ def test_random_cache_attend(i):
     o = oracle.BlockKVCacheOracle(shape, shape, 2, chunk, window, sink)
     g = torch.Generator().manual_seed(400 + i)
     steps = int(r.integers(1, 14))
+    Lq = int(r.choice([1, 3, chunk]))
+    # drawn after the case's other fields: causal attend, and the last chunk through the
+    # fused update + attend
+    causal = bool(r.random() < 0.4)
+    fused = bool(r.random() < 0.5)
     for idx in range(steps):
         k = torch.randn(B, Hkv, chunk, D, generator=g).to(dt)
         v = torch.randn(B, Hkv, chunk, D, generator=g).to(dt)
-        c.before_update(idx)
-        c.update(k.to(DEV), v.to(DEV))
         o.update(idx, k.float().numpy(), v.float().numpy())
-        c.after_update(idx)
-    Lq = int(r.choice([1, 3, chunk]))
+        c.before_update(idx)
+        if idx + 1 < steps or not fused:
+            c.update(k.to(DEV), v.to(DEV))
+            c.after_update(idx)
     q = torch.randn(B, Hkv * G, Lq, D, generator=g).to(dt)
     kv = torch.from_numpy(o.cached_k()).to(dt)
     vv = torch.from_numpy(o.cached_v()).to(dt)
+    if fused:
+        out = c.update_attend(k.to(DEV), v.to(DEV), q.to(DEV), is_causal=causal)
+        c.after_update(steps - 1)
+    else:
+        out = c.attend(q.to(DEV), is_causal=causal)
     assert torch.equal(c.cached_k().cpu(), kv)
-    ref, _ = oracle.sdpa(q, kv, vv, scale=np.float32(1 / np.sqrt(D)))
-    out = c.attend(q.to(DEV))
+    ref, _ = oracle.sdpa(q, kv, vv, is_causal=causal, scale=np.float32(1 / np.sqrt(D)),
+                         causal_align="bottom_right")
     assert_close(out, ref, dt, f"cache case {i}: sink={sink} window={window} chunk={chunk} "
-                               f"B={B} Hkv={Hkv} G={G} D={D} steps={steps} Lq={Lq}")
+                               f"B={B} Hkv={Hkv} G={G} D={D} steps={steps} Lq={Lq} "
+                               f"causal={causal} fused={fused}")

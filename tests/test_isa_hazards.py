@@ -57,7 +57,8 @@ def test_checker_separates_source_war_by_operand():
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
 @pytest.mark.parametrize("src_name, kernel", [("sdpa_bf16_d128_w64.hip", "attn_fwd_w_kernel"),
-                                              ("sdpa_bf16_d128_p.hip", "attn_fwd_p_kernel")])
+                                              ("sdpa_bf16_d128_p.hip", "attn_fwd_p_kernel"),
+                                              ("sdpa_f16_d64.hip", "attn_fwd_kernel")])
 def test_generated_code_has_no_inline_asm_hazards(tmp_path, src_name, kernel):
     from exact_attention_forward_flash_amd.build import HIPCC, flags_for, CSRC
     src = os.path.join(CSRC, src_name)
