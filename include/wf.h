@@ -255,8 +255,9 @@ int wf_block_kv_gather(const wf_block_kv_state* st, const wf_tensor* cache,
  * then the window from its oldest token) through the slot map of wf_block_kv_visible.
  *   q [B, Hq, Lq, Dk] (Hq a multiple of Hkv), out [B, Hq, Lq, Dv]; 16-bit dtypes with
  *   (Dk, Dv) in {(64,64), (128,128)}. scale as in wf_sdpa_fwd.
- *   is_causal 0: every query sees every visible token. 1: the Lq queries are the last Lq
- *     visible tokens (bottom-right: query i keeps visible token j iff j <= i + n_vis - Lq).
+ *   is_causal 0: every query sees every visible token (the page's attend). 1 (an addition
+ *     to the page's protocol): the Lq queries are the last Lq visible tokens (bottom-right:
+ *     query i keeps visible token j iff j <= i + n_vis - Lq).
  *   workspace: at least wf_block_kv_attend_workspace_size(...) bytes, 256-byte aligned;
  *   it holds per-split partial results (fp32) that a combine kernel merges. */
 size_t wf_block_kv_attend_workspace_size(const wf_block_kv_state* st, int B, int Hq, int Lq,
