@@ -166,18 +166,38 @@ __global__ __launch_bounds__(256) void split_combine_kernel(
   if (gid >= rows * d4) return;
   const int64_t row = gid / d4;
   const int d = (int)(gid % d4) * 4;
+  // Splits are read in batches of CB with every load of a batch issued before any is used
+  // (one memory round trip per batch instead of one per split); sums stay in split order.
+  constexpr int CB = 8;
   float mx = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) mx = fmaxf(mx, part_lse[s * rows + row]);
+  for (int s0 = 0; s0 < n_splits; s0 += CB) {
+    float ls[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      ls[u] = s0 + u < n_splits ? part_lse[(int64_t)(s0 + u) * rows + row] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) mx = fmaxf(mx, ls[u]);
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
   if (mx != -INFINITY) {
-    for (int s = 0; s < n_splits; ++s) {
-      const float ls = part_lse[s * rows + row];
-      const float wgt = __expf(ls - mx);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(part_o + (s * rows + row) * Dv + d);
-      den += wgt;
+    for (int s0 = 0; s0 < n_splits; s0 += CB) {
+      float ls[CB];
+      f32x4 o[CB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += wgt * o[e];
+      for (int u = 0; u < CB; ++u) {
+        const bool in = s0 + u < n_splits;
+        ls[u] = in ? part_lse[(int64_t)(s0 + u) * rows + row] : -INFINITY;
+        o[u] = in ? *reinterpret_cast<const f32x4*>(part_o + ((int64_t)(s0 + u) * rows + row) * Dv + d)
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const float wgt = __expf(ls[u] - mx);   // 0 past the last split
+        den += wgt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += wgt * o[u][e];
+      }
     }
   }
   const float inv = den > 0.f ? 1.0f / den : 0.f;
