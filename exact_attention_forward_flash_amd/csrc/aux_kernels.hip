@@ -244,25 +244,37 @@ template <> struct CopyUnit<2> { typedef uint16_t type; };
 
 // Copies one chunk of new rows into their slots, U bytes per thread. Segment 0 is K,
 // segment 1 is V (blockIdx.y). Strides are [b, h, row] in elements.
-template <int U>
+// Index arithmetic in I (32 bits when every index fits, which keeps the divisions cheap); the
+// ring slot of row r is the token itself inside the sink, else sink + (off0 + r) folded once
+// into the window, with off0 the window offset of the chunk's first token past the sink
+// (negative while the chunk still overlaps the sink).
+template <int U, typename I>
 __global__ __launch_bounds__(256) void kv_update_kernel(
     int esize, const char* k_new, int64_t kn0, int64_t kn1, int64_t kn2, const char* v_new,
     int64_t vn0, int64_t vn1, int64_t vn2, char* k_cache, int64_t kc0, int64_t kc1, int64_t kc2,
     char* v_cache, int64_t vc0, int64_t vc1, int64_t vc2, int B, int H, int chunk, int Dk, int Dv,
-    int64_t tok0, int64_t sink, int64_t window) {
+    int64_t tok0, int64_t sink, int64_t window, int64_t off0) {
   typedef typename CopyUnit<U>::type unit;
   const bool isv = blockIdx.y == 1;
   const int D = isv ? Dv : Dk;
   const int per_row = D * esize / U;
-  const int64_t n = (int64_t)B * H * chunk * per_row;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const I n = (I)B * H * chunk * per_row;
+  const I gid = (I)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n) return;
   const int piece = (int)(gid % per_row);
-  int64_t r = gid / per_row;
-  const int row = (int)(r % chunk); r /= chunk;
-  const int h = (int)(r % H);
-  const int b = (int)(r / H);
-  const int64_t slot = cache_slot(tok0 + row, sink, window);
+  const I r = gid / per_row;
+  const int row = (int)(r % chunk);
+  const I bh = r / chunk;
+  const int h = (int)(bh % H);
+  const int b = (int)(bh / H);
+  int64_t slot;
+  if (tok0 + row < sink) {
+    slot = tok0 + row;
+  } else {
+    int64_t x = off0 + row;
+    x = x >= window ? x - window : x;
+    slot = sink + x;
+  }
   const char* src = isv ? v_new + (b * vn0 + h * vn1 + row * vn2) * esize
                         : k_new + (b * kn0 + h * kn1 + row * kn2) * esize;
   char* dst = isv ? v_cache + (b * vc0 + h * vc1 + slot * vc2) * esize
@@ -279,15 +291,23 @@ hipError_t launch_kv_update(int unit, int esize, const void* k_new, const int64_
   const int64_t n = (int64_t)B * H * chunk * (Dmax * esize / unit);
   if (n == 0) return hipSuccess;
   const int blocks = (int)((n + 255) / 256);
-#define WF_UPD(U)                                                                            \
-  hipLaunchKernelGGL(kv_update_kernel<U>, dim3(blocks, 2), dim3(256), 0, s, esize,           \
+  const int64_t off0 = tok0 >= sink ? (tok0 - sink) % window : tok0 - sink;
+  const bool narrow = (int64_t)blocks * 256 < ((int64_t)1 << 31);
+#define WF_UPD(U, I)                                                                         \
+  hipLaunchKernelGGL((kv_update_kernel<U, I>), dim3(blocks, 2), dim3(256), 0, s, esize,      \
                      (const char*)k_new, kn_st[0], kn_st[1], kn_st[2], (const char*)v_new,   \
                      vn_st[0], vn_st[1], vn_st[2], (char*)k_cache, kc_st[0], kc_st[1],       \
                      kc_st[2], (char*)v_cache, vc_st[0], vc_st[1], vc_st[2], B, H, chunk, Dk, \
-                     Dv, tok0, sink, window)
-  if (unit == 16) WF_UPD(16);
-  else if (unit == 4) WF_UPD(4);
-  else WF_UPD(2);
+                     Dv, tok0, sink, window, off0)
+  if (narrow) {
+    if (unit == 16) WF_UPD(16, int);
+    else if (unit == 4) WF_UPD(4, int);
+    else WF_UPD(2, int);
+  } else {
+    if (unit == 16) WF_UPD(16, int64_t);
+    else if (unit == 4) WF_UPD(4, int64_t);
+    else WF_UPD(2, int64_t);
+  }
 #undef WF_UPD
   return hipGetLastError();
 }
