@@ -15,6 +15,8 @@ static const AttnEntry kTable[] = {
     // 8 waves (two per SIMD) on 256 query rows of one head: the block KV cache attend
     WF_ATTN_ENTRY(__bf16, DT_BF16, 64, 64, 64, 8, 1, MASK_NONE, false, MODE_SPLIT),
     WF_ATTN_ENTRY(__bf16, DT_BF16, 128, 128, 128, 8, 1, MASK_NONE, false, MODE_SPLIT),
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 64, 64, 64, 8, 1, MASK_NONE, true, MODE_SPLIT),
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 128, 128, 128, 8, 1, MASK_NONE, true, MODE_SPLIT),
 };
 #undef E
 // packed (query head, position) rows: the G*Lq queries of a KV head share one work item
@@ -30,6 +32,11 @@ const AttnEntry* attn_table_split_bf16(int* n) {
 static const AttnEntry kTableU[] = {
     U(64, 1, false),  U(64, 2, false),  U(64, 4, false),  U(64, 1, true),  U(64, 2, true),  U(64, 4, true),
     U(128, 1, false), U(128, 2, false), U(128, 4, false), U(128, 1, true), U(128, 2, true), U(128, 4, true),
+    // 8 waves on 256 query rows of one head
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 64, 64, 64, 8, 1, MASK_NONE, false, MODE_SPLITU),
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 64, 64, 64, 8, 1, MASK_NONE, true, MODE_SPLITU),
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 128, 128, 128, 8, 1, MASK_NONE, false, MODE_SPLITU),
+    WF_ATTN_ENTRY(__bf16, DT_BF16, 128, 128, 128, 8, 1, MASK_NONE, true, MODE_SPLITU),
 };
 #undef U
 const AttnEntry* attn_table_splitu_bf16(int* n) {

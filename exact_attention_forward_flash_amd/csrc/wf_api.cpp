@@ -1043,7 +1043,13 @@ static int attend_impl(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   const int64_t G = Hq / Hkv;
   const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
   const int causal = is_causal ? 1 : 0;
-  const int nw = (hpw == 1 && !causal && fu == nullptr && tune(T_ATTEND_NW) == 8) ? 8 : 4;
+  // One query head per KV head and more than 128 queries: 8-wave groups (256 query rows of
+  // one head, two waves per SIMD) share each K/V tile. Measured on the 256-query chunk over a
+  // 4k window (kernel trace of the 64-chunk stream): split kernel 24.8 us against 29.4 us
+  // with 4-wave groups (one wave per SIMD), combine 6.1 against 4.5 us (8 splits instead
+  // of 4). Fewer queries keep 4-wave groups (rows past Lq still run their MFMAs).
+  const int tnw = tune(T_ATTEND_NW);
+  const int nw = (hpw == 1 && (tnw == 8 || (tnw != 4 && Lq > 128))) ? 8 : 4;
   const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, nw, hpw, wf::MASK_NONE, causal,
                                      fu != nullptr ? wf::MODE_SPLITU : wf::MODE_SPLIT);
   if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
@@ -1053,8 +1059,9 @@ static int attend_impl(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   const int cus = cu_count();
   if (cus <= 0) return fail(WF_ERR_HIP, "cannot query the device's compute units");
   // About 3/4 of a work group per CU: measured on the 256-query chunk over a 4k window (256
-  // CUs), 192 groups run 20% faster than 512 (fewer fp32 partials to write and merge) and
-  // ~4% faster than 256.
+  // CUs), 4-wave groups: 192 run 20% faster than 512 (fewer fp32 partials to write and
+  // merge) and ~4% faster than 256; 8-wave groups: 192 (8 splits) as fast as 240 (10 splits,
+  // whose combine takes 1.4 us more), while 264 no longer fit in one round.
   int64_t target = std::max(1, cus * 3 / 4);
   if (tune(T_ATTEND_GROUPS) > 0) target = tune(T_ATTEND_GROUPS);
   int n_splits = (int)((target + base_blocks - 1) / base_blocks);

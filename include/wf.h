@@ -297,8 +297,9 @@ const char* wf_build_id(void);
  * "qpw" (32 | 64: queries per wave of the one-item-per-group kernels), "nw" (4: waves per
  * group of the 32-query kernel), "decode_pack" (0: no (head, position) row packing in wf_sdpa_decode), "decode_groups",
  * "decode_min_tiles" (split plan of wf_sdpa_decode), "mla_xcd" (0: no per-XCD split of the
- * MLA prefill), "attend_groups", "attend_nw", "attend_min_tiles" (split plan of
- * wf_block_kv_attend), "mask_pre" (0: masked calls without the lse keep Q as given and scale
+ * MLA prefill), "attend_groups", "attend_nw" (4 | 8: waves per group when each KV head
+ * has one query head), "attend_min_tiles" (split plan of wf_block_kv_attend and
+ * wf_block_kv_update_attend), "mask_pre" (0: masked calls without the lse keep Q as given and scale
  * every score in fp32). Changing a value while
  * another thread launches work races with that launch's choice (never with its result's
  * correctness). Returns WF_ERR_UNSUPPORTED for an unknown name, WF_ERR_NULL for a NULL

@@ -179,7 +179,8 @@ def test_snapshot_restore_continues_bit_identically():
 
 @pytest.mark.parametrize("sink,window,chunk,H,Hkv,dt", [
     (64, 448, 64, 2, 2, torch.float16), (0, 256, 64, 4, 1, torch.bfloat16),
-    (32, 96, 32, 8, 2, torch.float16), (256, 3840, 256, 4, 4, torch.float16)])
+    (32, 96, 32, 8, 2, torch.float16), (256, 3840, 256, 4, 4, torch.float16),
+    (128, 896, 256, 2, 2, torch.bfloat16)])
 def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H, Hkv, dt):
     """Causal attend (the chunk's queries are the newest visible tokens) across the roll of
     the window: only a kernel that reads the ring in chronological order matches the oracle's
@@ -214,7 +215,7 @@ def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H,
 
 @pytest.mark.parametrize("sink,window,chunk,H,Hkv,causal", [
     (64, 448, 64, 2, 2, False), (0, 256, 64, 4, 1, True), (256, 3840, 256, 24, 24, False),
-    (32, 96, 32, 8, 2, True)])
+    (32, 96, 32, 8, 2, True), (256, 768, 256, 4, 4, True)])
 def test_fused_update_attend_matches_the_two_calls(sink, window, chunk, H, Hkv, causal):
     """update_attend gives the output of update then attend (bit for bit when the attend takes
     the split kernel too; a non-causal attend over a single key split may take a dense kernel
