@@ -320,6 +320,9 @@ def main():
     ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
                     help="FETCH_SIZE, WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE counter CSVs "
                          "from rocprofv3 --pmc: record HBM bytes per launch and exit")
+    ap.add_argument("--tune", action="append", default=[], metavar="NAME=VALUE",
+                    help="run --workload under a launch-plan override of the library (wf_tune_set "
+                         "names, e.g. attend_nw=4); repeatable; other workloads only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 3 times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -337,8 +340,17 @@ def main():
     from synth import causal_gqa_prefill
 
     if args.workload != "causal_gqa":
-        other_workload(args.workload, args.steps, args.warmup)
+        plan = {}
+        for t in args.tune:
+            name, _, value = t.partition("=")
+            plan[name] = int(value)
+        with wf.tune(**plan):
+            other_workload(args.workload, args.steps, args.warmup)
         return
+    if args.tune:
+        print("--tune applies to the other workloads; the headline line runs the default plan",
+              file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         n = 256 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
