@@ -257,6 +257,45 @@ def other_workload(name, steps, warmup):
             tot_f += sum(e[0].elapsed_time(e[1]) for e in evs)
         line.update(fused_update_attend_ms_per_chunk=round(tot_f / reps / n, 4),
                     separate_update_plus_attend_ms_per_chunk=round((tot_u + tot_a) / reps / n, 4))
+
+        # The same 64-chunk streams captured once into HIP graphs and replayed: the library's
+        # calls enqueue kernels only, so a replay is the stream's launches without the host's
+        # per-call work between them (the per-call events above include any gap where the GPU
+        # waited for the host). tests/test_gpu_graph.py checks replays against eager runs.
+        def graph_of(fused):
+            cache = wf.BlockKVCache((B, H, sink + window, D), (B, H, sink + window, D), 2, C,
+                                    window, sink, device=dev)
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side), torch.cuda.graph(g, stream=side):
+                for c, q, k, v in chunks:
+                    cache.before_update(c)
+                    if fused:
+                        cache.update_attend(k, v, q, workspace=ws)
+                        cache.after_update(c)
+                    else:
+                        cache.update(k, v)
+                        cache.after_update(c)
+                        cache.attend(q, workspace=ws)
+            stream.wait_stream(side)
+            return g
+
+        g_reps = max(2, steps // 10)
+        for fused, key in ((False, "graph_update_plus_attend_ms_per_chunk"),
+                           (True, "graph_fused_update_attend_ms_per_chunk")):
+            g = graph_of(fused)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(g_reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            line[key] = round(e0.elapsed_time(e1) / g_reps / n, 4)
+            del g
+        line["graph_replays"] = g_reps
     elif name == "rope_gqa":
         import numpy as np
         w = synth.causal_gqa_prefill()

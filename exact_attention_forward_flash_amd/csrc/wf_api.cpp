@@ -1043,19 +1043,6 @@ static int attend_impl(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   const int64_t G = Hq / Hkv;
   const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
   const int causal = is_causal ? 1 : 0;
-  // One query head per KV head and more than 128 queries: 8-wave groups (256 query rows of
-  // one head, two waves per SIMD) share each K/V tile. Measured on the 256-query chunk over a
-  // 4k window (kernel trace of the 64-chunk stream): split kernel 24.8 us against 29.4 us
-  // with 4-wave groups (one wave per SIMD), combine 6.1 against 4.5 us (8 splits instead
-  // of 4). Fewer queries keep 4-wave groups (rows past Lq still run their MFMAs).
-  const int tnw = tune(T_ATTEND_NW);
-  const int nw = (hpw == 1 && (tnw == 8 || (tnw != 4 && Lq > 128))) ? 8 : 4;
-  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, nw, hpw, wf::MASK_NONE, causal,
-                                     fu != nullptr ? wf::MODE_SPLITU : wf::MODE_SPLIT);
-  if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
-  const int n_kt = (int)((n_vis + e->bn - 1) / e->bn);
-  const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
-  const int64_t base_blocks = (int64_t)n_qt * B * Hkv * (G / hpw);
   const int cus = cu_count();
   if (cus <= 0) return fail(WF_ERR_HIP, "cannot query the device's compute units");
   // About 3/4 of a work group per CU: measured on the 256-query chunk over a 4k window (256
@@ -1064,6 +1051,24 @@ static int attend_impl(const wf_block_kv_state* s, const wf_tensor* q, const wf_
   // whose combine takes 1.4 us more), while 264 no longer fit in one round.
   int64_t target = std::max(1, cus * 3 / 4);
   if (tune(T_ATTEND_GROUPS) > 0) target = tune(T_ATTEND_GROUPS);
+  const int64_t n_kt_all = (n_vis + 63) / 64;
+  // One query head per KV head and more than 128 queries: 8-wave groups (256 query rows of
+  // one head, two waves per SIMD) share each K/V tile. Measured on the 256-query chunk over a
+  // 4k window (kernel trace of the 64-chunk stream): split kernel 24.8 us against 29.4 us
+  // with 4-wave groups (one wave per SIMD), combine 6.1 against 4.5 us (8 splits instead
+  // of 4). Fewer queries keep 4-wave groups (rows past Lq still run their MFMAs), and so do
+  // short caches where the 8-wave plan would give each split a single key tile (the first
+  // chunks of that stream: 18-19 us against 14 us).
+  const int tnw = tune(T_ATTEND_NW);
+  const int64_t groups8 = ((Lq + 255) / 256) * B * Hkv;
+  const bool long8 = n_kt_all >= 2 * std::min<int64_t>(n_kt_all, (target + groups8 - 1) / groups8);
+  const int nw = (hpw == 1 && (tnw == 8 || (tnw != 4 && Lq > 128 && long8))) ? 8 : 4;
+  const wf::AttnEntry* e = find_attn(dt, (int)D, (int)D, (int)Dv, nw, hpw, wf::MASK_NONE, causal,
+                                     fu != nullptr ? wf::MODE_SPLITU : wf::MODE_SPLIT);
+  if (!e) return fail(WF_ERR_UNSUPPORTED, "split kernel not built");
+  const int n_kt = (int)((n_vis + e->bn - 1) / e->bn);
+  const int n_qt = (int)((Lq + e->bmp - 1) / e->bmp);
+  const int64_t base_blocks = (int64_t)n_qt * B * Hkv * (G / hpw);
   int n_splits = (int)((target + base_blocks - 1) / base_blocks);
   if (n_splits > kMaxSplits) n_splits = kMaxSplits;
   if (n_splits > n_kt) n_splits = n_kt;

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from exact_attention_forward_flash_amd import BlockKVCache, ChunkOrderError
+from exact_attention_forward_flash_amd import BlockKVCache, ChunkOrderError, tune
 from synth import cache_stream_chunks
 from tests.parity import assert_close, to64
 
@@ -181,11 +181,20 @@ def test_snapshot_restore_continues_bit_identically():
     (64, 448, 64, 2, 2, torch.float16), (0, 256, 64, 4, 1, torch.bfloat16),
     (32, 96, 32, 8, 2, torch.float16), (256, 3840, 256, 4, 4, torch.float16),
     (128, 896, 256, 2, 2, torch.bfloat16)])
-def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H, Hkv, dt):
+@pytest.mark.parametrize("nw", [-1, 8])
+def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H, Hkv, dt, nw):
     """Causal attend (the chunk's queries are the newest visible tokens) across the roll of
     the window: only a kernel that reads the ring in chronological order matches the oracle's
     causal attention over its token list once the ring has wrapped; the non-causal attend
-    of the same chunk is checked too, and a single new query as in decoding."""
+    of the same chunk is checked too, and a single new query as in decoding. nw=8 forces the
+    8-wave split groups (automatic only for many heads over long caches) where they apply."""
+    if nw == 8 and (chunk <= 128 or H != Hkv):
+        pytest.skip("8-wave groups take one query head per KV head and more than 128 queries")
+    with tune(attend_nw=nw):
+        _causal_attend_case(sink, window, chunk, H, Hkv, dt)
+
+
+def _causal_attend_case(sink, window, chunk, H, Hkv, dt):
     D = 64 if chunk < 256 else 128
     shape = (1, Hkv, sink + window, D)
     c = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=dt)
@@ -216,11 +225,19 @@ def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H,
 @pytest.mark.parametrize("sink,window,chunk,H,Hkv,causal", [
     (64, 448, 64, 2, 2, False), (0, 256, 64, 4, 1, True), (256, 3840, 256, 24, 24, False),
     (32, 96, 32, 8, 2, True), (256, 768, 256, 4, 4, True)])
-def test_fused_update_attend_matches_the_two_calls(sink, window, chunk, H, Hkv, causal):
+@pytest.mark.parametrize("nw", [-1, 8])
+def test_fused_update_attend_matches_the_two_calls(sink, window, chunk, H, Hkv, causal, nw):
     """update_attend gives the output of update then attend (bit for bit when the attend takes
     the split kernel too; a non-causal attend over a single key split may take a dense kernel
     instead, which rounds differently) and leaves the same cache contents, across the roll of
-    the window and a repeated chunk."""
+    the window and a repeated chunk; nw=8 forces the 8-wave split groups where they apply."""
+    if nw == 8 and (chunk <= 128 or H != Hkv):
+        pytest.skip("8-wave groups take one query head per KV head and more than 128 queries")
+    with tune(attend_nw=nw):
+        _fused_case(sink, window, chunk, H, Hkv, causal)
+
+
+def _fused_case(sink, window, chunk, H, Hkv, causal):
     D = 128
     shape = (1, Hkv, sink + window, D)
     a = BlockKVCache(shape, shape, 2, chunk, window, sink, device=DEV, dtype=torch.float16)
