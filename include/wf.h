@@ -27,6 +27,10 @@
  *     aligned (a multiple of 8 elements for 16-bit data, 4 for fp32).
  *   - Results are deterministic: the same inputs give bit-identical outputs on every run
  *     (no atomics in any reduction; fixed split and combine order).
+ *   - A call enqueues kernel launches only (no memset, copy, allocation or host wait), so a
+ *     sequence of calls may be captured into a HIP graph and replayed; the kernel arguments
+ *     are fixed at capture, and so are the host-side cache state changes a captured block
+ *     KV cache call makes (a replay repeats the captured chunks).
  */
 #ifndef WF_H_
 #define WF_H_
