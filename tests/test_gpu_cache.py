@@ -177,19 +177,18 @@ def test_snapshot_restore_continues_bit_identically():
     assert torch.isfinite(outs_b[-1].float()).all()
 
 
-@pytest.mark.parametrize("sink,window,chunk,H,Hkv,dt", [
-    (64, 448, 64, 2, 2, torch.float16), (0, 256, 64, 4, 1, torch.bfloat16),
-    (32, 96, 32, 8, 2, torch.float16), (256, 3840, 256, 4, 4, torch.float16),
-    (128, 896, 256, 2, 2, torch.bfloat16)])
-@pytest.mark.parametrize("nw", [-1, 8])
+@pytest.mark.parametrize("sink,window,chunk,H,Hkv,dt,nw", [
+    (64, 448, 64, 2, 2, torch.float16, -1), (0, 256, 64, 4, 1, torch.bfloat16, -1),
+    (32, 96, 32, 8, 2, torch.float16, -1), (256, 3840, 256, 4, 4, torch.float16, -1),
+    (128, 896, 256, 2, 2, torch.bfloat16, -1),
+    (256, 3840, 256, 4, 4, torch.float16, 8), (128, 896, 256, 2, 2, torch.bfloat16, 8)])
 def test_causal_attend_reads_keys_in_chronological_order(sink, window, chunk, H, Hkv, dt, nw):
     """Causal attend (the chunk's queries are the newest visible tokens) across the roll of
     the window: only a kernel that reads the ring in chronological order matches the oracle's
     causal attention over its token list once the ring has wrapped; the non-causal attend
     of the same chunk is checked too, and a single new query as in decoding. nw=8 forces the
-    8-wave split groups (automatic only for many heads over long caches) where they apply."""
-    if nw == 8 and (chunk <= 128 or H != Hkv):
-        pytest.skip("8-wave groups take one query head per KV head and more than 128 queries")
+    8-wave split groups (one query head per KV head, more than 128 queries; automatic only
+    for many heads over long caches)."""
     with tune(attend_nw=nw):
         _causal_attend_case(sink, window, chunk, H, Hkv, dt)
 
@@ -222,17 +221,15 @@ def _causal_attend_case(sink, window, chunk, H, Hkv, dt):
         c.after_update(idx)
 
 
-@pytest.mark.parametrize("sink,window,chunk,H,Hkv,causal", [
-    (64, 448, 64, 2, 2, False), (0, 256, 64, 4, 1, True), (256, 3840, 256, 24, 24, False),
-    (32, 96, 32, 8, 2, True), (256, 768, 256, 4, 4, True)])
-@pytest.mark.parametrize("nw", [-1, 8])
+@pytest.mark.parametrize("sink,window,chunk,H,Hkv,causal,nw", [
+    (64, 448, 64, 2, 2, False, -1), (0, 256, 64, 4, 1, True, -1), (256, 3840, 256, 24, 24, False, -1),
+    (32, 96, 32, 8, 2, True, -1), (256, 768, 256, 4, 4, True, -1),
+    (256, 3840, 256, 24, 24, False, 8), (256, 768, 256, 4, 4, True, 8)])
 def test_fused_update_attend_matches_the_two_calls(sink, window, chunk, H, Hkv, causal, nw):
     """update_attend gives the output of update then attend (bit for bit when the attend takes
     the split kernel too; a non-causal attend over a single key split may take a dense kernel
     instead, which rounds differently) and leaves the same cache contents, across the roll of
-    the window and a repeated chunk; nw=8 forces the 8-wave split groups where they apply."""
-    if nw == 8 and (chunk <= 128 or H != Hkv):
-        pytest.skip("8-wave groups take one query head per KV head and more than 128 queries")
+    the window and a repeated chunk; nw=8 forces the 8-wave split groups."""
     with tune(attend_nw=nw):
         _fused_case(sink, window, chunk, H, Hkv, causal)
 
