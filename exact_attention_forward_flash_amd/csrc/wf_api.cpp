@@ -176,9 +176,9 @@ const wf::AttnEntry* find_attn(int dtype, int dqk, int dqk1, int dv, int nw, int
   return nullptr;
 }
 
-const wf::F32Entry* find_f32(int dqk, int dv, int mask, int causal) {
+const wf::F32Entry* find_f32(int dqk, int dv, int mask, int causal, bool ks = false) {
   int n = 0;
-  const wf::F32Entry* t = wf::attn_table_f32(&n);
+  const wf::F32Entry* t = ks ? wf::attn_table_f32_ks(&n) : wf::attn_table_f32(&n);
   for (int i = 0; i < n; ++i)
     if (t[i].dqk == dqk && t[i].dv == dv && t[i].mask == mask && t[i].causal == causal) return &t[i];
   return nullptr;
@@ -315,7 +315,10 @@ int run_dense(const wf_tensor* q, const wf_tensor* k, const wf_tensor* v, const 
   a.inv_scale = 1.0f / scale;
   const int dt = kernel_dtype(q->dtype);
   if (dt == wf::DT_F32) {
-    const wf::F32Entry* e = find_f32(Dqk, Dv, mask_kind, causal);
+    // One 32-query tile per (batch, head) over more than one 32-key tile: the key-split form
+    // (its four waves share the key tiles instead of three of them idling).
+    const bool ks = Lq <= 32 && Lk > 32;
+    const wf::F32Entry* e = find_f32(Dqk, Dv, mask_kind, causal, ks);
     if (!e) return fail(WF_ERR_UNSUPPORTED, "no fp32 kernel for Dqk=%d Dv=%d", Dqk, Dv);
     a.n_qtiles = (Lq + e->bm - 1) / e->bm;
     const int64_t blocks = (int64_t)a.n_qtiles * B * Hq;

@@ -90,6 +90,8 @@ struct F32Entry {
   int bm;  // queries per work group
 };
 const F32Entry* attn_table_f32(int* n);
+// key-split form for one 32-query tile per (batch, head)
+const F32Entry* attn_table_f32_ks(int* n);
 
 // Rotary embedding pass (rope.hip): one tensor's input strides, contiguous output, shape and
 // first position.

@@ -111,7 +111,11 @@ def test_value_width_differs_from_key_width(case):
 
 
 F32_CASES = [(2, 4, 2, 33, 50, 64, 96, False), (1, 4, 4, 130, 70, 128, 128, True),
-             (2, 2, 1, 64, 64, 64, 64, True), (1, 2, 2, 5, 300, 128, 64, False)]
+             (2, 2, 1, 64, 64, 64, 64, True), (1, 2, 2, 5, 300, 128, 64, False),
+             # one 32-query tile per head over several key tiles: the key-split fp32 form
+             (2, 4, 2, 32, 48, 64, 96, False), (1, 4, 4, 1, 200, 128, 128, True),
+             (1, 2, 1, 17, 129, 64, 64, False), (2, 2, 2, 32, 1000, 128, 96, False),
+             (1, 4, 2, 32, 33, 128, 128, True)]
 
 
 @pytest.mark.parametrize("case", F32_CASES, ids=[str(c) for c in F32_CASES])
@@ -132,6 +136,8 @@ MASK_CASES = [  # dtype, mask kind, mask broadcast shape, Lq, Lk, D
     ("bf16", "f32", "11", 128, 128, 128),
     ("fp32", "bool", "b1", 70, 90, 64),
     ("fp32", "f32", "bh", 33, 130, 128),
+    ("fp32", "bool", "bh", 20, 200, 64),      # key-split fp32 form (Lq <= 32, several key tiles)
+    ("fp32", "f32", "b1", 32, 97, 128),
 ]
 
 
@@ -155,6 +161,29 @@ def test_masks(case):
     out = run(w)
     ref, _ = oracle.sdpa(w["q"], w["k"], w["v"], mask=w["mask"], scale=np.float32(w["scale"]))
     assert_close(out, ref, w["q"].dtype, str(case))
+
+
+def test_fp32_key_split_lse_and_masked_rows():
+    """The key-split fp32 form merges the partial (m, l, O) of its four waves: the lse, rows
+    whose kept keys all fall in one wave's tiles, and rows with no kept key (output 0, lse
+    -inf) against the oracle."""
+    B, H, Lq, Lk, D = 2, 3, 24, 260, 64
+    w = random_sdpa_inputs(B, H, H, Lq, Lk, D, D, "fp32", seed=21)
+    g = torch.Generator().manual_seed(22)
+    keep = torch.rand((B, H, Lq, Lk), generator=g) < 0.5
+    keep[:, :, 3] = False                  # no kept key
+    keep[:, :, 5] = False
+    keep[:, :, 5, 40:60] = True            # kept keys only in the tile of the second wave
+    keep[:, :, 7] = False
+    keep[:, :, 7, 258] = True              # one kept key, in the last (partial) tile
+    w["mask"] = keep
+    out, lse = run(w, return_lse=True)
+    ref, ref_lse = oracle.sdpa(w["q"], w["k"], w["v"], mask=keep, scale=np.float32(w["scale"]))
+    assert_close(out, ref, torch.float32, "key-split fp32")
+    live = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(to64(lse)), live)
+    assert np.abs(to64(lse)[live] - ref_lse[live]).max() < 1e-4
+    assert (to64(out)[:, :, 3] == 0).all() and (to64(out)[:, :, 5] != 0).any()
 
 
 def test_fully_masked_rows_and_empty_keys():
