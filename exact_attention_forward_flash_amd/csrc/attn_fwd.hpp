@@ -402,6 +402,9 @@ struct AttnFwd {
       const int e = lim < 0 ? 0 : lim / BN + 1;
       kt_live = e < kt_live ? e : kt_live;
     }
+    // A wave whose rows all lie past the item's last query (the end of a sequence or of Lq)
+    // computes nothing: no tile of it is live.
+    if (!PACK && qlo >= it.Lq) kt_live = it.kt_lo;
     if (kt_live < it.kt_lo) kt_live = it.kt_lo;
 
     // ---- operand fragments from LDS ----------------------------------------------------
