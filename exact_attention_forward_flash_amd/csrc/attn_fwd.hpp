@@ -726,11 +726,34 @@ struct AttnFwd {
         wait_vmem();
         __syncthreads();
       };
-      for (int u = 0;;) {
-        iter(u, sK1, sK0, sV0, sV1, sc, sn);  // even tiles: scores in sc, next in sn
-        if (++u >= n_tiles) break;
-        iter(u, sK0, sK1, sV1, sV0, sn, sc);  // odd tiles: roles swapped
-        if (++u >= n_tiles) break;
+      if constexpr (MODE != MODE_SPLIT && MODE != MODE_SPLITU) {
+        for (int u = 0;;) {
+          iter(u, sK1, sK0, sV0, sV1, sc, sn);  // even tiles: scores in sc, next in sn
+          if (++u >= n_tiles) break;
+          iter(u, sK0, sK1, sV1, sV0, sn, sc);  // odd tiles: roles swapped
+          if (++u >= n_tiles) break;
+        }
+      } else {
+        // Split-KV groups (one item each, few tiles): the last tile computes no next S^T
+        // (there is none), and nothing follows it that needs the wait and barrier. (The other
+        // one-item modes keep the uniform loop: this second tail spills registers in some of
+        // their instantiations.)
+        auto last = [&](const WF_LDS char* Vc, f32x16* cur, f32x16* nxt) {
+          if (n_tiles - 1 < n_live) {
+            rescale(mt_cur, cur);
+            phase_a(sK0, std::false_type(), cur, nxt);
+            phase_b(Vc, std::false_type(), nxt);
+          }
+        };
+        const int n_main = n_tiles - 1;
+        for (int u = 0; u < n_main;) {
+          iter(u, sK1, sK0, sV0, sV1, sc, sn);
+          if (++u >= n_main) break;
+          iter(u, sK0, sK1, sV1, sV0, sn, sc);
+          if (++u >= n_main) break;
+        }
+        if (n_main & 1) last(sV1, sn, sc);
+        else last(sV0, sc, sn);
       }
     }
 
