@@ -726,7 +726,7 @@ struct AttnFwd {
         wait_vmem();
         __syncthreads();
       };
-      if constexpr (MODE != MODE_SPLIT && MODE != MODE_SPLITU) {
+      if constexpr (MODE != MODE_SPLIT && MODE != MODE_SPLITU && MODE != MODE_VARLEN) {
         for (int u = 0;;) {
           iter(u, sK1, sK0, sV0, sV1, sc, sn);  // even tiles: scores in sc, next in sn
           if (++u >= n_tiles) break;
@@ -734,15 +734,20 @@ struct AttnFwd {
           if (++u >= n_tiles) break;
         }
       } else {
-        // Split-KV groups (one item each, few tiles): the last tile computes no next S^T
-        // (there is none), and nothing follows it that needs the wait and barrier. (The other
-        // one-item modes keep the uniform loop: this second tail spills registers in some of
-        // their instantiations.)
+        // Split-KV groups and the varlen items: an item's last tile computes no next S^T
+        // (there is none); split groups end there without the wait and barrier, varlen groups
+        // keep them for the next item. (The dense modes keep the uniform loop: this second
+        // tail spills registers in some of their instantiations.)
         auto last = [&](const WF_LDS char* Vc, f32x16* cur, f32x16* nxt) {
           if (n_tiles - 1 < n_live) {
             rescale(mt_cur, cur);
             phase_a(sK0, std::false_type(), cur, nxt);
             phase_b(Vc, std::false_type(), nxt);
+          }
+          if constexpr (MODE == MODE_VARLEN) {
+            // the group's next item refills the buffers: every wave must be done with them
+            wait_vmem();
+            __syncthreads();
           }
         };
         const int n_main = n_tiles - 1;
