@@ -12,9 +12,8 @@
 //   * Q of the next item is loaded into registers one item ahead; in the last iteration of
 //     an item the S^T of the next item's first tile is computed with it (that tile's
 //     scores and max are ready when the item starts);
-//   * an item's output is normalised and stored after the last iteration's barrier (turned
-//     around in the wave's Q staging area so that every store writes whole rows), and those
-//     stores complete during the next iteration.
+//   * an item's output is normalised and stored after the last iteration's barrier, and
+//     those stores complete during the next iteration.
 //
 // Items (batch, KV head, HPW query heads, BMP query positions) are those of the one-item-
 // per-group launch. Work group p of P (P a multiple of 8) takes the items of its XCD (the
@@ -519,45 +518,29 @@ struct AttnFwdP {
       mt_cur = xhalf_max(fmaxf(mx[0], mx[1])) * cs;
     };
 
-    // Output of an item: O / l rounded to the input type, rows past Lq dropped; the
-    // log-sum-exp when asked for. The wave's 32 x DV tile is turned around in its Q staging
-    // area (free from the item's last read_q until the next stage_q): row j, 16-byte chunk
-    // (4n + q4) ^ (j % OCH) holds head-dim 32n + 8q4 .. +7 (each half-wave writes 8 bytes of
-    // it), then copy i stores rows i * 64 / OCH + lane / OCH, chunk lane % OCH, so that every
-    // store writes whole rows instead of 8-byte pieces of 32 rows (all eight waves store at
-    // once: the scattered form held each item switch for about 6k cycles).
-    static_assert(DV == DQK, "the output tile fits the Q staging area");
-    constexpr int OCH = DV / 8;   // 16-byte chunks per output row (a power of two)
+    // Output of an item: O / l, rows past Lq dropped; the log-sum-exp when asked for.
     auto store_item = [&](const Item& it) {
       const float l = xhalf_sum(l_run);
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       const int hq = it.hq0 + hw;
-      typedef T t4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-      for (int n = 0; n < NDV; ++n)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          t4 o4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[n][4 * q4 + e] * inv);
-          *reinterpret_cast<WF_LDS t4*>(sQw + j * OCH * 16 + (((4 * n + q4) ^ (j & (OCH - 1))) * 16) + 8 * hf) = o4;
-        }
       const int qrow = it.pos0 + qw + j;
-      if (a.lse != nullptr && hf == 0 && qrow < a.Lq) {
-        const float lse2 = l > 0.f ? (m_run == -INFINITY ? 0.f : m_run) + __builtin_log2f(l) : -INFINITY;
-        a.lse[((int64_t)it.b * a.Hq + hq) * a.Lq + qrow] = lse2 * kLn2;
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own rows, read back below
-      T* obase = (T*)a.o + it.b * a.o_sb + hq * a.o_sh;
-      const int ch = lane & (OCH - 1);
+      if (qrow < a.Lq) {
+        T* dst = (T*)a.o + it.b * a.o_sb + hq * a.o_sh + (int64_t)qrow * a.o_sm;
+        typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-      for (int i = 0; i < 32 * OCH / 64; ++i) {
-        const int row = i * (64 / OCH) + lane / OCH;
-        const u32x4 v16 = lds_read16(sQw + row * OCH * 16 + ((ch ^ (row & (OCH - 1))) * 16));
-        const int orow = it.pos0 + qw + row;
-        if (orow < a.Lq) *reinterpret_cast<u32x4*>(obase + (int64_t)orow * a.o_sm + 8 * ch) = v16;
+        for (int n = 0; n < NDV; ++n)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            t4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = (T)(oacc[n][4 * q4 + e] * inv);
+            *reinterpret_cast<t4*>(dst + 32 * n + 8 * q4 + 4 * hf) = o4;
+          }
+        if (a.lse != nullptr && hf == 0) {
+          const float lse2 = l > 0.f ? (m_run == -INFINITY ? 0.f : m_run) + __builtin_log2f(l) : -INFINITY;
+          a.lse[((int64_t)it.b * a.Hq + hq) * a.Lq + qrow] = lse2 * kLn2;
+        }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // done with the area before it is restaged
     };
 
     // ---- start: the first item's Q and first tiles; then the second item's Q is staged ----
@@ -588,18 +571,16 @@ struct AttnFwdP {
     // Iteration g reads K_{g+1} (S^T of the next tile) and V_g, and copies K_{g+2} and
     // V_{g+1} meanwhile. u is the current tile's index within its item. In an item's last
     // iteration the next tile is the next item's first: its Q^T is read from the staging
-    // area (filled during the item); after that iteration's barrier the item's O passes
-    // through the area on its way out, and then the item after the next one is staged.
+    // area (filled during the item), and the item after it is staged.
     int u = 0;
     bool done = false;
     auto iter = [&](const WF_LDS char* Kn, WF_LDS char* Kfill, const WF_LDS char* Vc,
                     WF_LDS char* Vfill, f32x16* cur, f32x16* nxt) {
       const bool last = u + 1 == cur_it.n;
       if (last) {
-        // The next item's Q was staged at the previous item switch, after that item's O left
-        // the area; a one-tile item reads it at once, so its wave waits for the loads first.
-        if (u == 0) wait_vmem();
         read_q(nxt_it);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_q(item_at(list, cur_it.k + 2));
       }
       rescale(mt_cur, cur);
       phase_a(Kn, Vc, cur, nxt, Kfill);   // copies K_{g+2} into Kfill on the way
@@ -621,7 +602,6 @@ struct AttnFwdP {
         l_run = 0.f;
         cur_it = nxt_it;
         nxt_it = item_at(list, cur_it.k + 1);
-        stage_q(nxt_it);
         u = 0;
         done = cur_it.n == 0;
       } else {
