@@ -1,5 +1,7 @@
 // Auxiliary kernels: the varlen tile schedule, the split-KV combine and the block KV cache
 // copy / gather.
+#include <type_traits>
+
 #include "wf_internal.hpp"
 
 namespace wf {
@@ -155,17 +157,20 @@ hipError_t launch_varlen_schedule(const int32_t* q_seqlen, const int32_t* kv_seq
 // where O_s is split s's normalised partial output and lse_s its log-sum-exp. A query with
 // no kept key in any split gets 0. Splits are summed in index order (deterministic).
 // ------------------------------------------------------------------------------------------
-template <typename T>
+// Index arithmetic in I: 32 bits whenever rows * Dv/4 fits (the divisions that split a thread
+// index into row, batch and head are then a few instructions instead of a 64-bit division
+// sequence each); element offsets stay 64-bit.
+template <typename T, typename I>
 __global__ __launch_bounds__(256) void split_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int n_splits,
     int B, int Hq, int Lq, int Dv, T* out, int64_t o_sb, int64_t o_sh, int64_t o_sm,
     float* lse) {
   const int64_t rows = (int64_t)B * Hq * Lq;
-  const int d4 = Dv / 4;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= rows * d4) return;
-  const int64_t row = gid / d4;
-  const int d = (int)(gid % d4) * 4;
+  const I d4 = (I)(Dv / 4);
+  const I gid = (I)blockIdx.x * (I)blockDim.x + (I)threadIdx.x;
+  if ((int64_t)gid >= rows * d4) return;
+  const I row = gid / d4;
+  const int d = (int)(gid - row * d4) * 4;
   // Splits are read in batches of CB with every load of a batch issued before any is used
   // (one memory round trip per batch instead of one per split); sums stay in split order.
   constexpr int CB = 8;
@@ -203,9 +208,11 @@ __global__ __launch_bounds__(256) void split_combine_kernel(
   const float inv = den > 0.f ? 1.0f / den : 0.f;
   // lse of the whole row: the splits' lse merged the same way (-inf when no key is kept)
   if (lse != nullptr && d == 0) lse[row] = den > 0.f ? mx + __logf(den) : -INFINITY;
-  const int q = (int)(row % Lq);
-  const int hq = (int)((row / Lq) % Hq);
-  const int b = (int)(row / ((int64_t)Lq * Hq));
+  const I bh = row / (I)Lq;
+  const int q = (int)(row - bh * (I)Lq);
+  const I b_ = bh / (I)Hq;
+  const int hq = (int)(bh - b_ * (I)Hq);
+  const int b = (int)b_;
   T* dst = out + b * o_sb + hq * o_sh + (int64_t)q * o_sm + d;
 #pragma unroll
   for (int e = 0; e < 4; ++e) dst[e] = (T)(acc[e] * inv);
@@ -217,15 +224,20 @@ hipError_t launch_split_combine(int dtype, const float* part_o, const float* par
                                 hipStream_t s) {
   const int64_t n = (int64_t)B * Hq * Lq * (Dv / 4);
   const int blocks = (int)((n + 255) / 256);
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(split_combine_kernel<__bf16>, dim3(blocks), dim3(256), 0, s, part_o,
-                       part_lse, n_splits, B, Hq, Lq, Dv, (__bf16*)out, o_sb, o_sh, o_sm, lse);
-  else if (dtype == DT_F16)
-    hipLaunchKernelGGL(split_combine_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, part_o,
-                       part_lse, n_splits, B, Hq, Lq, Dv, (_Float16*)out, o_sb, o_sh, o_sm, lse);
-  else
-    hipLaunchKernelGGL(split_combine_kernel<float>, dim3(blocks), dim3(256), 0, s, part_o,
-                       part_lse, n_splits, B, Hq, Lq, Dv, (float*)out, o_sb, o_sh, o_sm, lse);
+  const bool i32 = (int64_t)blocks * 256 < ((int64_t)1 << 31);
+  auto go = [&](auto tag, auto* o) {
+    typedef decltype(tag) I;
+    typedef typename std::remove_pointer<decltype(o)>::type T;
+    hipLaunchKernelGGL((split_combine_kernel<T, I>), dim3(blocks), dim3(256), 0, s, part_o,
+                       part_lse, n_splits, B, Hq, Lq, Dv, o, o_sb, o_sh, o_sm, lse);
+  };
+  auto by_index = [&](auto* o) {
+    if (i32) go(uint32_t(0), o);
+    else go(int64_t(0), o);
+  };
+  if (dtype == DT_BF16) by_index((__bf16*)out);
+  else if (dtype == DT_F16) by_index((_Float16*)out);
+  else by_index((float*)out);
   return hipGetLastError();
 }
 
